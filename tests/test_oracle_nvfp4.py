@@ -1,0 +1,139 @@
+"""Pins for the oracle's NVFP4 record: exact two-level grid values, scale
+read-back at the bytes the page fixes, power-of-two invariance, the
+subnormal-group-scale failure mode the per-token scale removes, and the MLA
+decode against a brute-force loop."""
+import json
+import math
+import os
+
+import numpy as np
+
+from oracle.codecs import e4m3_decode, e2m1_decode, bf16_round
+from oracle.nvfp4 import (encode_records, decode_records, record_s2, mla_decode, new_pool,
+                          store_records, RECORD_BYTES, OFF_GSCALE, OFF_S2, OFF_ROPE)
+from workloads import make_mla_case
+from workloads.gen import mla_layer_stds
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")
+
+
+def token(rng, std, n=1):
+    return bf16_round((rng.standard_normal((n, 576)) * std).astype(np.float32))
+
+
+def test_record_geometry_matches_page():
+    with open(GOLDEN) as f:
+        g = json.load(f)["nvfp4_record"]
+    assert RECORD_BYTES == g["record_bytes"]
+    assert [OFF_S2, OFF_S2 + 4] == g["s2_offset"]
+    rec = encode_records(token(np.random.default_rng(0), 1.0, 4))
+    assert rec.shape == (4, 368)
+    assert np.all(rec[:, 288:292] == 0) and np.all(rec[:, 296:304] == 0)
+
+
+def test_exact_grid_token_amax_168():
+    # amax 168 -> s2 = 168/2688 = 2^-4 exactly; the top group's scale is 448
+    # (code 0x7E) and dg = 28, so e2m1 multiples of 28 round-trip exactly.
+    x = np.zeros((1, 576), np.float32)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    x[0, 0:16] = np.tile(grid, 2) * 28.0
+    x[0, 3] = -1.5 * 28.0
+    # group 1: amax 0.75 -> ratio 0.75 / (6 * 2^-4) = 2 (on the e4m3 grid),
+    # dg = 2 * 2^-4 = 0.125
+    x[0, 16:32] = np.tile(grid, 2) * 0.125
+    x[0, 0] = 168.0
+    x[0, 0:16] = np.where(np.arange(16) == 0, 168.0, x[0, 0:16])
+    rec = encode_records(x)
+    assert record_s2(rec)[0] == np.float32(2.0 ** -4)
+    assert rec[0, OFF_GSCALE] == 0x7E
+    assert e4m3_decode(rec[0, OFF_GSCALE + 1]) == 2.0
+    lat, rope = decode_records(rec)
+    assert np.array_equal(lat[0, :32], x[0, :32].astype(np.float64))
+    assert np.all(lat[0, 32:] == 0) and np.all(rope == 0)
+    # all-zero token: zero scale, zero codes
+    z = encode_records(np.zeros((1, 576), np.float32))
+    assert np.all(z == 0)
+
+
+def test_power_of_two_invariance():
+    rng = np.random.default_rng(1)
+    x = token(rng, 1.3, 64)
+    base = encode_records(x)
+    for k in (-5, -1, 3):
+        xs = (x * np.float32(2.0 ** k)).astype(np.float32)
+        r = encode_records(xs, rope_scale=2.0 ** k)
+        assert np.array_equal(r[:, :OFF_S2], base[:, :OFF_S2])
+        assert np.array_equal(r[:, OFF_S2 + 4:], base[:, OFF_S2 + 4:])
+        assert np.array_equal(record_s2(r), (record_s2(base) * np.float32(2.0 ** k)))
+
+
+def test_s2_readback_and_error_bound():
+    rng = np.random.default_rng(2)
+    x = token(rng, 0.7, 200)
+    rec = encode_records(x)
+    amax = np.max(np.abs(x[:, :512]), axis=1)
+    assert np.array_equal(record_s2(rec), (amax / np.float32(2688)).astype(np.float32))
+    lat, _ = decode_records(rec)
+    # each element is within one e2m1 step (<= 2 * dg) of its input and within
+    # half a step where the group scale leaves headroom: |err| <= dg
+    gsc = e4m3_decode(rec[:, OFF_GSCALE:OFF_GSCALE + 32]) * record_s2(rec)[:, None]
+    dg = np.repeat(gsc, 16, axis=1)
+    err = np.abs(lat - x[:, :512])
+    # (the reciprocal-multiply can land a value a hair past a tie: 1 + 2^-20)
+    assert np.all(err <= dg * (1.0 + 2.0 ** -20))
+
+
+def test_no_subnormal_group_scales_on_layer_std_range():
+    # With the per-token outer scale no group scale lands in e4m3 subnormals,
+    # the failure mode of a static outer scale of 1.0 on shallow layers.
+    rng = np.random.default_rng(3)
+    for std in mla_layer_stds():
+        x = token(rng, std, 256)
+        sg = encode_records(x)[:, OFF_GSCALE:OFF_GSCALE + 32]
+        assert not np.any((sg & 0x78) == 0), std       # exponent field 0 = subnormal/zero
+    # the static reading (outer scale 1) at std 0.05: a third of the group
+    # scales ag / 6 fall below 2^-6, the e4m3 subnormal range
+    x = token(rng, 0.05, 256)
+    ag = np.max(np.abs(x[:, :512].reshape(256, 32, 16)), axis=2)
+    assert np.mean(ag / 6.0 < 2.0 ** -6) > 0.25
+
+
+def test_rope_part_uses_e4m3_store_quantizer():
+    rng = np.random.default_rng(4)
+    x = token(rng, 3.0, 8)
+    rec = encode_records(x, rope_scale=0.5)
+    from oracle.kvcache import quantize_e4m3
+    assert np.array_equal(rec[:, OFF_ROPE:], quantize_e4m3(x[:, 512:], 0.5))
+
+
+def test_mla_decode_matches_bruteforce():
+    c = make_mla_case("m", 5, [20, 33], num_q_heads=3, layer_std=0.8)
+    pool = new_pool(c.num_pages)
+    store_records(pool, c.kv.float().numpy(), c.slot_mapping, 1.25)
+    q = c.q.float().numpy()
+    out = mla_decode(q, pool, c.block_table, c.seq_lens, c.softmax_scale, 1.25)
+    start = 0
+    for b, L in enumerate(c.seq_lens):
+        L = int(L)
+        rec = encode_records(c.kv.float().numpy()[start:start + L], 1.25)
+        s2 = record_s2(rec)
+        for h in range(3):
+            scores, vals = [], []
+            for j in range(L):
+                codes = []
+                for byte in rec[j, :256]:
+                    codes += [byte & 0xF, byte >> 4]
+                gs = e4m3_decode(rec[j, 256:288])
+                lat = [float(e2m1_decode(codes[d])) * float(gs[d // 16]) * float(s2[j])
+                       for d in range(512)]
+                rp = [float(e4m3_decode(rec[j, 304 + d])) * 1.25 for d in range(64)]
+                s = sum(float(q[b, h, d]) * lat[d] for d in range(512))
+                s += sum(float(q[b, h, 512 + d]) * rp[d] for d in range(64))
+                scores.append(s * c.softmax_scale)
+                vals.append(lat)
+            mx = max(scores)
+            w = [math.exp(s - mx) for s in scores]
+            tot = sum(w)
+            want = [sum(w[j] * vals[j][d] for j in range(L)) / tot for d in range(512)]
+            assert np.max(np.abs(out[b, h] - np.array(want))) < 1e-12
+        start += L
