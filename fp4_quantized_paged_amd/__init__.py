@@ -1,0 +1,242 @@
+"""kvq: quantized-KV-cache attention for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libkvq.so`` (include/kvq.h). It only
+marshals arguments: torch tensors provide device memory and the current HIP
+stream, every step of the computation runs in the library's HIP kernels.
+There is no CPU fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvq.so")
+
+FMT_E4M3 = 1
+FMT_NVFP4_MLA368 = 2
+PAGE_SIZE = 16
+RECORD_BYTES = 368
+
+STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
+          -3: "KVQ_ERR_BAD_SCALE", -4: "KVQ_ERR_WORKSPACE", -5: "KVQ_ERR_HIP"}
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (where, STATUS.get(status, status), status_str(status)))
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p)]
+
+
+class AttnParams(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("num_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("q_scale", ctypes.c_float),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("alibi_slopes", ctypes.c_void_p)]
+
+
+_lib = None
+
+_SIGNATURES = {
+    "kvq_abi_version": (ctypes.c_int, []),
+    "kvq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "kvq_store": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p, ctypes.c_int64,
+                                 ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                 ctypes.c_float, ctypes.c_float, ctypes.c_void_p]),
+    "kvq_calibrate_amax": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p]),
+    "kvq_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), ctypes.c_int32,
+                                                     ctypes.c_int32, ctypes.POINTER(AttnParams)]),
+    "kvq_paged_attn_decode": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                             ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.POINTER(AttnParams), ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "kvq_paged_attn_prefill": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                              ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.POINTER(AttnParams), ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvq.so once. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libkvq.so not found at %s: build it with "
+                               "`python -m fp4_quantized_paged_amd.build`" % LIB_PATH)
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_str(status: int) -> str:
+    try:
+        return lib().kvq_status_str(int(status)).decode()
+    except Exception:  # pragma: no cover - only when the library is absent
+        return "?"
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise KvqError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("kvq needs device tensors")
+
+
+class E4M3Cache:
+    """Paged e4m3 K/V pools: K u8 [pages][Hkv][16][D], V u8 [pages][Hkv][D][16]."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int,
+                 device="cuda", fill: int = 0x7F):
+        self.num_pages, self.num_kv_heads, self.head_dim = num_pages, num_kv_heads, head_dim
+        self.k = torch.full((num_pages, num_kv_heads, PAGE_SIZE, head_dim), fill,
+                            dtype=torch.uint8, device=device)
+        self.v = torch.full((num_pages, num_kv_heads, head_dim, PAGE_SIZE), fill,
+                            dtype=torch.uint8, device=device)
+
+    @property
+    def desc(self) -> CacheDesc:
+        return CacheDesc(FMT_E4M3, PAGE_SIZE, self.num_kv_heads, self.head_dim,
+                         self.num_pages, self.k.data_ptr(), self.v.data_ptr())
+
+
+class Nvfp4Cache:
+    """Paged NVFP4 MLA records: u8 [pages][16][368]."""
+
+    def __init__(self, num_pages: int, device="cuda", fill: int = 0x7F):
+        self.num_pages = num_pages
+        self.records = torch.full((num_pages, PAGE_SIZE, RECORD_BYTES), fill, dtype=torch.uint8,
+                                  device=device)
+
+    @property
+    def desc(self) -> CacheDesc:
+        return CacheDesc(FMT_NVFP4_MLA368, PAGE_SIZE, 1, 576, self.num_pages,
+                         self.records.data_ptr(), None)
+
+
+def store(cache, k: torch.Tensor, v: Optional[torch.Tensor], slot_mapping: torch.Tensor,
+          k_scale: float, v_scale: float = 1.0) -> None:
+    """kvq_store. E4M3: k, v bf16 [T, Hkv, D]; NVFP4: k bf16 [T, 576], v None
+    and k_scale the RoPE scale. slot_mapping int64 [T] (negative: skip)."""
+    _need_cuda(k, v, slot_mapping)
+    assert slot_mapping.dtype == torch.int64 and k.dtype == torch.bfloat16
+    d = cache.desc
+    T = k.shape[0]
+    st = lib().kvq_store(ctypes.byref(d), _ptr(k), k.stride(0), _ptr(v),
+                         v.stride(0) if v is not None else 0, _ptr(slot_mapping), T,
+                         float(k_scale), float(v_scale), _stream())
+    _check(st, "kvq_store")
+
+
+def calibrate_amax(x: torch.Tensor, slot_mapping: Optional[torch.Tensor] = None,
+                   amax: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None):
+    """kvq_calibrate_amax over the rows of x (bf16, first dim = rows, the rest
+    flattened). Returns (amax, scale) as 1-element device fp32 tensors; pass
+    ``amax`` to keep a running value."""
+    _need_cuda(x, slot_mapping)
+    assert x.dtype == torch.bfloat16
+    rows = x.shape[0]
+    row_len = 1
+    for n in x.shape[1:]:
+        row_len *= int(n)
+    x2 = x.reshape(rows, row_len)
+    if amax is None:
+        amax = torch.zeros(1, dtype=torch.float32, device=x.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    st = lib().kvq_calibrate_amax(_ptr(x2), rows, row_len, x2.stride(0) if rows else row_len,
+                                  _ptr(slot_mapping), _ptr(amax), _ptr(scale), _stream())
+    _check(st, "kvq_calibrate_amax")
+    return amax, scale
+
+
+def _params(num_q_heads, softmax_scale, q_scale, k_scale, v_scale, window, slopes, num_splits):
+    return AttnParams(int(num_q_heads), int(window), int(num_splits), 0, float(softmax_scale),
+                      float(q_scale), float(k_scale), float(v_scale), _ptr(slopes))
+
+
+def decode_workspace_bytes(cache, num_seqs: int, max_seq_len: int, num_q_heads: int,
+                           window: int = 0, num_splits: int = 0, softmax_scale: float = 1.0) -> int:
+    d = cache.desc
+    p = _params(num_q_heads, softmax_scale, 1.0, 1.0, 1.0, window, None, num_splits)
+    return int(lib().kvq_decode_workspace_bytes(ctypes.byref(d), int(num_seqs), int(max_seq_len),
+                                                ctypes.byref(p)))
+
+
+def decode(cache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+           max_seq_len: int, softmax_scale: float, q_scale: float = 1.0, k_scale: float = 1.0,
+           v_scale: float = 1.0, window: int = 0, slopes: Optional[torch.Tensor] = None,
+           num_splits: int = 0, out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """kvq_paged_attn_decode. q bf16 [B, Hq, Dqk] -> out bf16 [B, Hq, Dv]."""
+    _need_cuda(q, block_table, seq_lens, slopes)
+    assert q.dtype == torch.bfloat16 and q.is_contiguous()
+    assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    B, Hq, _ = q.shape
+    d = cache.desc
+    dv = 512 if d.format == FMT_NVFP4_MLA368 else d.head_dim
+    if out is None:
+        out = torch.empty((B, Hq, dv), dtype=torch.bfloat16, device=q.device)
+    p = _params(Hq, softmax_scale, q_scale, k_scale, v_scale, window, slopes, num_splits)
+    need = int(lib().kvq_decode_workspace_bytes(ctypes.byref(d), B, int(max_seq_len), ctypes.byref(p)))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().kvq_paged_attn_decode(ctypes.byref(d), _ptr(q), _ptr(block_table),
+                                     block_table.stride(0), _ptr(seq_lens), B, int(max_seq_len),
+                                     ctypes.byref(p), _ptr(out), _ptr(workspace), ws_bytes,
+                                     _stream())
+    _check(st, "kvq_paged_attn_decode")
+    return out
+
+
+def prefill(cache, q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,
+            block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+            softmax_scale: float, q_scale: float = 1.0, k_scale: float = 1.0,
+            v_scale: float = 1.0, window: int = 0, slopes: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """kvq_paged_attn_prefill. q bf16 [sumQ, Hq, D] -> out bf16 [sumQ, Hq, D]."""
+    _need_cuda(q, cu_q_lens, block_table, seq_lens, slopes)
+    assert q.dtype == torch.bfloat16 and q.is_contiguous()
+    total_q, Hq, D = q.shape
+    d = cache.desc
+    if out is None:
+        out = torch.empty((total_q, Hq, D), dtype=torch.bfloat16, device=q.device)
+    p = _params(Hq, softmax_scale, q_scale, k_scale, v_scale, window, slopes, 0)
+    st = lib().kvq_paged_attn_prefill(ctypes.byref(d), _ptr(q), _ptr(cu_q_lens), total_q,
+                                      int(max_q_len), _ptr(block_table), block_table.stride(0),
+                                      _ptr(seq_lens), int(seq_lens.shape[0]), int(max_seq_len),
+                                      ctypes.byref(p), _ptr(out), None, 0, _stream())
+    _check(st, "kvq_paged_attn_prefill")
+    return out

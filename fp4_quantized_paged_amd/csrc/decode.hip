@@ -1,0 +1,359 @@
+// fp8 (e4m3) paged decode attention: split-KV kernel and split combine.
+//
+// What is computed (vLLM PR 54705, "Purpose", query-quantization and
+// descale-handling bullets): Q is quantized to e4m3 with its per-tensor scale;
+// raw scores are e4m3 dot products; the QK descale is folded into the softmax
+// scale and the exact bf16 relative bias is added after it; the V descale
+// multiplies the output. Online softmax across key blocks follows the
+// evidence document's "Tier 0" (P in fp8, pre-scaled by 2^8 so its largest
+// value 256 stays below the e4m3 maximum; rescaling is exact here, i.e. a
+// threshold of 0).
+//
+// Kernel design (gfx950, wave64):
+//  * one workgroup per (sequence, KV head, 16-row query tile, split), with W
+//    waves that take interleaved 128-key blocks (8 pages) of the split;
+//  * QK^T: per block, eight v_mfma_f32_16x16x128_f8f6f4 with A = 16 key rows
+//    (K = head_dim) and B = the 16 query rows of the GQA group. The key row
+//    each lane loads is permuted so that the output lane holding query row
+//    (l % 16) receives exactly the 32 keys of pages {2g, 2g+1} of the block,
+//    g = l / 16: that is the B-operand slice PV needs, so P never leaves the
+//    registers;
+//  * PV: A = V^T, read straight from the token-minor V pages (16 contiguous
+//    bytes per dim per page), B = P. P = 256 * p is split into two e4m3 terms
+//    (hi = e4m3(P), lo = e4m3(P - hi)) accumulated by two MFMAs, which keeps
+//    the relative error of each weight near 2^-8 while staying on fp8 MFMA;
+//  * every lane loads its MFMA operand bytes directly from HBM with 16-byte
+//    loads (the cache layout makes each operand slice contiguous), so there
+//    is no LDS staging in the key loop; LDS is used once, to merge the waves;
+//  * W waves merge through LDS; with one split the workgroup writes bf16 out
+//    directly, otherwise (m, l, o) partials go to the workspace and the
+//    combine kernel merges them.
+#include "kvq_device.h"
+#include "kvq_launch.h"
+
+namespace kvq {
+
+namespace {
+
+template <int D>
+struct DecodeTile {
+  static constexpr int kTiles = D / 16;   // 16-dim output tiles
+};
+
+// Byte mask (0xFF per kept byte) of the 16 tokens of a page: tokens whose
+// absolute position lies in [lo, hi) are kept.
+__device__ __forceinline__ void page_byte_mask(int page_pos0, int lo, int hi, uint32_t m[4]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int p = page_pos0 + 4 * w + b;
+      v |= (p >= lo && p < hi) ? (0xFFu << (8 * b)) : 0u;
+    }
+    m[w] = v;
+  }
+}
+
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_e4m3_kernel(DecodeE4M3Launch a, int splits,
+                                                            int blocks_per_split, int qtiles) {
+  constexpr int kTiles = DecodeTile<D>::kTiles;
+  extern __shared__ __align__(16) float smem[];   // [max(W/2,1)][16][D] o, [W][16] m, [W][16] l
+  float *s_o = smem;
+  float *s_m = smem + (W > 1 ? W / 2 : 1) * 16 * D;
+  float *s_l = s_m + W * 16;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row = lane & 15;      // query row (B/N index) and A-row index
+  const int grp = lane >> 4;      // K-slice / key-group index
+
+  int idx = blockIdx.x;
+  const int split = idx % splits;
+  idx /= splits;
+  const int qt = idx % qtiles;
+  idx /= qtiles;
+  const int g = idx % a.hkv;
+  const int b = idx / a.hkv;
+
+  const int group = a.hq / a.hkv;
+  const int qrow = qt * 16 + row;
+  const bool qvalid = qrow < group;
+  const int head = g * group + (qvalid ? qrow : 0);
+
+  const int L = a.seq_lens[b];
+  const int lo = a.window > 0 ? max(0, L - a.window) : 0;
+  const int page_lo = lo >> 4;
+  const int page_hi = (L + 15) >> 4;
+  const int nblk = (page_hi - page_lo + 7) >> 3;
+  const int blk_begin = split * blocks_per_split;
+  const int blk_end = min(nblk, blk_begin + blocks_per_split);
+
+  // ---- Q: quantize this lane's 32 dims of its query row to e4m3
+  v8i qop = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (qvalid && (D == 128 || grp < 2)) {
+    const uint4 *qp = (const uint4 *)(a.q + ((size_t)b * a.hq + head) * D + grp * 32);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint2 w = quant8_e4m3(qp[c], a.q_inv);
+      qop[2 * c] = (int)w.x;
+      qop[2 * c + 1] = (int)w.y;
+    }
+  }
+  const float slope = (a.slopes != nullptr && qvalid) ? a.slopes[head] : 0.0f;
+  const bool has_bias = a.slopes != nullptr;
+  const float qpos = (float)(L - 1);
+
+  float m_run = -INFINITY;   // running max, log2 domain
+  float l_run = 0.0f;        // this lane's partial sum of p
+  v4f o[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const size_t kv_head_stride = (size_t)16 * D;               // bytes per head-page
+  const size_t page_stride = (size_t)a.hkv * kv_head_stride;  // bytes per page
+  const int32_t *bt = a.block_table + (size_t)b * a.bt_stride;
+
+  for (int blk = blk_begin + wave; blk < blk_end; blk += W) {
+    const int pbase = page_lo + blk * 8;
+    // pages this lane touches: K rows come from pages pbase + 2*(row/4) + {0,1},
+    // V columns (and this lane's output keys) from pages pbase + 2*grp + {0,1}
+    const int kp0 = pbase + 2 * (row >> 2);
+    const int vp0 = pbase + 2 * grp;
+    const bool kv0 = kp0 < page_hi, kv1 = kp0 + 1 < page_hi;
+    const bool vv0 = vp0 < page_hi, vv1 = vp0 + 1 < page_hi;
+    const int kphys0 = kv0 ? bt[kp0] : 0;
+    const int kphys1 = kv1 ? bt[kp0 + 1] : 0;
+    const int vphys0 = vv0 ? bt[vp0] : 0;
+    const int vphys1 = vv1 ? bt[vp0 + 1] : 0;
+
+    // ---- K operands: MFMA j takes token 4*(j%4) + (row%4) of page (j<4 ? kp0 : kp0+1)
+    v8i kop[8];
+    const bool kload = (D == 128 || grp < 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool valid = (j < 4 ? kv0 : kv1) && kload;
+      const int phys = j < 4 ? kphys0 : kphys1;
+      const int tok = 4 * (j & 3) + (row & 3);
+      if (valid) {
+        const uint4 *src = (const uint4 *)(a.kc + (size_t)phys * page_stride + (size_t)g * kv_head_stride +
+                                           (size_t)tok * D + grp * 32);
+        const uint4 x0 = src[0], x1 = src[1];
+        kop[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      } else {
+        kop[j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+    // ---- V^T operands: tile t, dim 16t + row, 16 tokens of vp0 then of vp0+1
+    v8i vop[kTiles];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      const int dim = 16 * t + row;
+      uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
+      if (vv0) x0 = *(const uint4 *)(a.vc + (size_t)vphys0 * page_stride + (size_t)g * kv_head_stride + (size_t)dim * 16);
+      if (vv1) x1 = *(const uint4 *)(a.vc + (size_t)vphys1 * page_stride + (size_t)g * kv_head_stride + (size_t)dim * 16);
+      vop[t] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    }
+
+    // ---- S^T = K Q^T: lane holds keys (vp0 + j/4, token 4*(j%4) + i) of query row
+    v4f sacc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sacc[j] = mfma_16x16x128_e4m3(kop[j], qop, v4f{0.f, 0.f, 0.f, 0.f});
+
+    // ---- scores (log2 domain), masking, block max
+    const int kpos0 = vp0 * 16;   // absolute position of this lane's first key
+    float x[8][4];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kpos = kpos0 + 16 * (j >> 2) + 4 * (j & 3) + i;
+        float s = sacc[j][i] * a.fold_log2;
+        if (has_bias) {
+          const float bias = round_bf16_finite(slope * ((float)kpos - qpos));
+          s = fmaf(bias, kLog2e, s);
+        }
+        s = (kpos >= lo && kpos < L) ? s : -INFINITY;
+        x[j][i] = s;
+        bmax = fmaxf(bmax, s);
+      }
+    }
+    bmax = wave_max_xor(bmax, 16);
+    bmax = wave_max_xor(bmax, 32);
+    const float m_new = fmaxf(m_run, bmax);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+
+    // ---- P = 2^8 p as two e4m3 terms
+    v8i phi, plo;
+    float psum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float p[4], h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(x[j][i] - m_use);
+        psum += p[i];
+        p[i] *= 256.0f;
+      }
+      const uint32_t hi = cvt4_e4m3(p[0], p[1], p[2], p[3]);
+      const v2f h01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+      const v2f h23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+      h[0] = h01.x; h[1] = h01.y; h[2] = h23.x; h[3] = h23.y;
+      phi[j] = (int)hi;
+      plo[j] = (int)cvt4_e4m3(p[0] - h[0], p[1] - h[1], p[2] - h[2], p[3] - h[3]);
+    }
+    l_run = l_run * alpha + psum;
+
+    // ---- zero V bytes of tokens outside [lo, L) on partial pages (they may
+    // hold stale or NaN bytes, and 0 * NaN would poison the MFMA)
+    const bool edge = (pbase * 16 < lo) || ((pbase + 8) * 16 > L);
+    if (edge) {
+      uint32_t m0[4], m1[4];
+      page_byte_mask(vp0 * 16, lo, L, m0);
+      page_byte_mask(vp0 * 16 + 16, lo, L, m1);
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          vop[t][w] &= (int)m0[w];
+          vop[t][w + 4] &= (int)m1[w];
+        }
+      }
+    }
+
+    // ---- O^T = V^T P^T, rescaled by alpha first
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      o[t] *= alpha;
+      o[t] = mfma_16x16x128_e4m3(vop[t], phi, o[t]);
+      o[t] = mfma_16x16x128_e4m3(vop[t], plo, o[t]);
+    }
+  }
+
+  // ---- per-row sum of p across the four key groups
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+
+  // ---- merge the W waves through LDS (fixed order: deterministic).
+  // Lane holds O[query row][dims 16t + 4*grp + i]. Every wave first rescales
+  // to the workgroup max, then waves [H, W) hand their O to waves [0, H),
+  // which add it and publish the H partial sums.
+  if (grp == 0) {
+    s_m[wave * 16 + row] = m_run;
+    s_l[wave * 16 + row] = l_run;
+  }
+  __syncthreads();
+  {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w * 16 + row]);
+    const float f = __builtin_amdgcn_exp2f(m_run - (M == -INFINITY ? 0.0f : M));
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) o[t] *= f;
+  }
+  constexpr int H = W > 1 ? W / 2 : 1;
+  if (W > 1) {
+    if (wave >= H) {
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t)
+        *(v4f *)(s_o + ((size_t)(wave - H) * 16 + row) * D + 16 * t + 4 * grp) = o[t];
+    }
+    __syncthreads();
+    if (wave < H) {
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t)
+        o[t] += *(const v4f *)(s_o + ((size_t)wave * 16 + row) * D + 16 * t + 4 * grp);
+    }
+    __syncthreads();
+  }
+  if (wave < H) {
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t)
+      *(v4f *)(s_o + ((size_t)wave * 16 + row) * D + 16 * t + 4 * grp) = o[t];
+  }
+  __syncthreads();
+
+  const int rows_here = min(16, group - qt * 16);
+  for (int e = threadIdx.x; e < rows_here * D; e += 64 * W) {
+    const int r = e / D;
+    const int dcol = e - r * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w * 16 + r]);
+    const float Mu = M == -INFINITY ? 0.0f : M;
+    float acc = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int w = 0; w < H; ++w) acc += s_o[((size_t)w * 16 + r) * D + dcol];
+#pragma unroll
+    for (int w = 0; w < W; ++w) den += __builtin_amdgcn_exp2f(s_m[w * 16 + r] - Mu) * s_l[w * 16 + r];
+    const int h = g * group + qt * 16 + r;
+    if (splits == 1) {
+      const float val = den > 0.0f ? (acc / den) * (a.v_scale * (1.0f / 256.0f)) : 0.0f;
+      a.out[((size_t)b * a.hq + h) * D + dcol] = (uint16_t)f32_to_bf16_bits(val);
+    } else {
+      const size_t pi = ((size_t)b * a.hq + h) * splits + split;
+      a.part_o[pi * D + dcol] = acc * (1.0f / 256.0f);
+      if (dcol == 0) {
+        a.part_ml[2 * pi] = M;
+        a.part_ml[2 * pi + 1] = den;
+      }
+    }
+  }
+}
+
+// Merge split partials: out = v_scale * sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(const float *part_o, const float *part_ml,
+                                                            uint16_t *out, int splits, float v_scale) {
+  const int bh = blockIdx.x;          // b * hq + h
+  const int dcol = threadIdx.x;
+  const float *ml = part_ml + (size_t)bh * splits * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[2 * s]);
+  const float Mu = M == -INFINITY ? 0.0f : M;
+  float acc = 0.0f, den = 0.0f;
+  const float *po = part_o + (size_t)bh * splits * D + dcol;
+  for (int s = 0; s < splits; ++s) {
+    const float f = __builtin_amdgcn_exp2f(ml[2 * s] - Mu);
+    acc += f * po[(size_t)s * D];
+    den += f * ml[2 * s + 1];
+  }
+  const float val = den > 0.0f ? (acc / den) * v_scale : 0.0f;
+  out[(size_t)bh * D + dcol] = (uint16_t)f32_to_bf16_bits(val);
+}
+
+template <int D, int W>
+hipError_t launch_decode_t(const DecodeE4M3Launch &a, const DecodePlan &p, hipStream_t s) {
+  const size_t grid = (size_t)a.batch * a.hkv * p.qtiles * p.splits;
+  const size_t lds = sizeof(float) * ((size_t)(W > 1 ? W / 2 : 1) * 16 * D + 2 * W * 16);
+  hipLaunchKernelGGL((decode_e4m3_kernel<D, W>), dim3((unsigned)grid), dim3(64 * W), lds, s, a,
+                     p.splits, p.blocks_per_split, p.qtiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)((size_t)a.batch * a.hq)), dim3(D), 0, s,
+                     a.part_o, a.part_ml, a.out, p.splits, a.v_scale);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_d(const DecodeE4M3Launch &a, const DecodePlan &p, hipStream_t s) {
+  switch (p.waves) {
+    case 1: return launch_decode_t<D, 1>(a, p, s);
+    case 2: return launch_decode_t<D, 2>(a, p, s);
+    case 4: return launch_decode_t<D, 4>(a, p, s);
+    default: return launch_decode_t<D, 8>(a, p, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_e4m3(const DecodeE4M3Launch &a, const DecodePlan &p, hipStream_t s) {
+  if (a.d == 64) return launch_decode_d<64>(a, p, s);
+  return launch_decode_d<128>(a, p, s);
+}
+
+}  // namespace kvq

@@ -1,0 +1,100 @@
+// Internal launch interface between the C-ABI layer (kvq_api.cpp) and the
+// kernel translation units. Host code only; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+struct StoreE4M3Launch {
+  const uint16_t *k, *v;
+  int64_t k_stride, v_stride;  // elements between tokens
+  const int64_t *slot;
+  int64_t num_tokens;
+  uint8_t *kc, *vc;
+  int hkv, d;
+  float k_inv, v_inv;          // fp32(1/scale), computed on the host
+};
+hipError_t launch_store_e4m3(const StoreE4M3Launch &a, hipStream_t s);
+
+struct StoreNvfp4Launch {
+  const uint16_t *x;           // [T][576] bf16
+  int64_t stride;
+  const int64_t *slot;
+  int64_t num_tokens;
+  uint8_t *records;            // [pages][16][368]
+  float rope_inv;              // fp32(1/rope_scale)
+};
+hipError_t launch_store_nvfp4(const StoreNvfp4Launch &a, hipStream_t s);
+
+struct AmaxLaunch {
+  const uint16_t *x;
+  int64_t rows, row_len, row_stride;
+  const int64_t *slot;
+  float *amax_inout;
+  float *scale_out;
+};
+hipError_t launch_amax(const AmaxLaunch &a, int num_cus, hipStream_t s);
+
+// Split plan of the e4m3 decode kernel.
+struct DecodePlan {
+  int waves;        // waves per workgroup (1, 2, 4 or 8)
+  int splits;       // KV splits per (sequence, KV head, query tile)
+  int blocks_per_split;  // 128-key blocks (8 pages) per split
+  int qtiles;       // ceil(group / 16)
+  size_t workspace; // bytes of partials (0 when splits == 1)
+};
+
+struct DecodeE4M3Launch {
+  const uint16_t *q;           // [B][Hq][D]
+  const uint8_t *kc, *vc;
+  const int32_t *block_table;
+  int64_t bt_stride;
+  const int32_t *seq_lens;
+  const float *slopes;         // [Hq] or nullptr
+  uint16_t *out;               // [B][Hq][D]
+  float *part_o;               // [B][Hq][S][D]
+  float *part_ml;              // [B][Hq][S][2]
+  int batch, hq, hkv, d, window;
+  float q_inv;                 // fp32(1/q_scale)
+  float fold_log2;             // softmax_scale * q_scale * k_scale * log2(e)
+  float v_scale;
+};
+hipError_t launch_decode_e4m3(const DecodeE4M3Launch &a, const DecodePlan &p, hipStream_t s);
+
+struct PrefillE4M3Launch {
+  const uint16_t *q;           // [total_q][Hq][D]
+  const int32_t *cu_q_lens;
+  const uint8_t *kc, *vc;
+  const int32_t *block_table;
+  int64_t bt_stride;
+  const int32_t *seq_lens;
+  const float *slopes;
+  uint16_t *out;
+  int batch, hq, hkv, d, window, max_q_len;
+  float q_inv, fold_log2, v_scale;
+};
+hipError_t launch_prefill_e4m3(const PrefillE4M3Launch &a, hipStream_t s);
+
+struct DecodeMlaLaunch {
+  const uint16_t *q;           // [B][Hq][576]
+  const uint8_t *records;
+  const int32_t *block_table;
+  int64_t bt_stride;
+  const int32_t *seq_lens;
+  uint16_t *out;               // [B][Hq][512]
+  float *part_o;               // [B][Hq][S][512]
+  float *part_ml;              // [B][Hq][S][2]
+  int batch, hq;
+  float scale_log2;            // softmax_scale * log2(e)
+  float rope_scale;
+};
+struct MlaPlan {
+  int splits;
+  int pages_per_split;
+  size_t workspace;
+};
+hipError_t launch_decode_mla(const DecodeMlaLaunch &a, const MlaPlan &p, hipStream_t s);
+
+}  // namespace kvq

@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched):
+the library loads, exports every function include/kvq.h declares, and
+rejects bad arguments with the documented status before touching the GPU."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import fp4_quantized_paged_amd as kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+FAKE = 0x100000  # a 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kvq.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"kvq_store", "kvq_calibrate_amax", "kvq_paged_attn_decode",
+            "kvq_paged_attn_prefill"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.kvq_abi_version() == 1
+    for s in (0, -1, -2, -3, -4, -5):
+        assert lib.kvq_status_str(s)
+
+
+def e4m3_desc(**kw):
+    d = dict(format=1, page_size=16, num_kv_heads=4, head_dim=128, num_pages=64, k=FAKE, v=FAKE)
+    d.update(kw)
+    return kvq.CacheDesc(d["format"], d["page_size"], d["num_kv_heads"], d["head_dim"],
+                         d["num_pages"], d["k"], d["v"])
+
+
+def params(**kw):
+    p = dict(num_q_heads=32, window=0, num_splits=0, reserved=0, softmax_scale=0.088,
+             q_scale=1.0, k_scale=1.0, v_scale=1.0, alibi_slopes=None)
+    p.update(kw)
+    return kvq.AttnParams(p["num_q_heads"], p["window"], p["num_splits"], p["reserved"],
+                          p["softmax_scale"], p["q_scale"], p["k_scale"], p["v_scale"],
+                          p["alibi_slopes"])
+
+
+def store(lib, desc, T=4, ks=1.0, vs=1.0, k=FAKE, v=FAKE, stride=512, slot=FAKE):
+    return lib.kvq_store(ctypes.byref(desc), k, stride, v, stride, slot, T, ks, vs, None)
+
+
+def test_store_validation(lib):
+    assert lib.kvq_store(None, FAKE, 512, FAKE, 512, FAKE, 4, 1.0, 1.0, None) == -1
+    assert store(lib, e4m3_desc(format=3)) == -2          # e.g. e5m2 / FNUZ: unknown format
+    assert store(lib, e4m3_desc(format=0)) == -2
+    assert store(lib, e4m3_desc(page_size=32)) == -2
+    assert store(lib, e4m3_desc(head_dim=96)) == -2
+    assert store(lib, e4m3_desc(k=None)) == -1
+    assert store(lib, e4m3_desc(k=FAKE + 4)) == -1          # misaligned pool
+    for bad in (0.0, -1.0, math.nan, math.inf):
+        assert store(lib, e4m3_desc(), ks=bad) == -3
+        assert store(lib, e4m3_desc(), vs=bad) == -3
+    assert store(lib, e4m3_desc(), stride=500) == -1      # stride below one token
+    assert store(lib, e4m3_desc(), stride=516) == -1      # not a multiple of 8
+    assert store(lib, e4m3_desc(), T=-1) == -1
+    assert store(lib, e4m3_desc(), slot=None) == -1
+    assert store(lib, e4m3_desc(), T=0) == 0              # zero tokens: no launch
+    nv = kvq.CacheDesc(2, 16, 1, 576, 64, FAKE, None)
+    assert lib.kvq_store(ctypes.byref(nv), FAKE, 576, FAKE, 0, FAKE, 4, 1.0, 1.0, None) == -1
+    assert lib.kvq_store(ctypes.byref(nv), FAKE, 576, None, 0, FAKE, 0, 1.0, 1.0, None) == 0
+    assert lib.kvq_store(ctypes.byref(nv), FAKE, 576, None, 0, FAKE, 4, 0.0, 1.0, None) == -3
+    bad_nv = kvq.CacheDesc(2, 16, 1, 512, 64, FAKE, None)
+    assert lib.kvq_store(ctypes.byref(bad_nv), FAKE, 576, None, 0, FAKE, 4, 1.0, 1.0, None) == -2
+
+
+def test_calibrate_validation(lib):
+    f = lib.kvq_calibrate_amax
+    assert f(FAKE, 10, 512, 512, None, None, None, None) == -1     # no amax buffer
+    assert f(FAKE, 10, 500, 512, None, FAKE, None, None) == -1     # row_len % 8
+    assert f(FAKE, 10, 512, 256, None, FAKE, None, None) == -1     # stride < row_len
+    assert f(None, 10, 512, 512, None, FAKE, None, None) == -1
+    assert f(FAKE + 2, 10, 512, 512, None, FAKE, None, None) == -1  # misaligned
+
+
+def decode(lib, desc, p, B=2, max_len=100, ws=None, ws_bytes=0, bt_stride=64, q=FAKE):
+    return lib.kvq_paged_attn_decode(ctypes.byref(desc), q, FAKE, bt_stride, FAKE, B, max_len,
+                                     ctypes.byref(p), FAKE, ws, ws_bytes, None)
+
+
+def test_decode_validation(lib):
+    d = e4m3_desc()
+    assert decode(lib, d, params(num_q_heads=30)) == -1          # Hq % Hkv != 0
+    assert decode(lib, d, params(window=-1)) == -1
+    assert decode(lib, d, params(reserved=1)) == -1
+    for bad in (0.0, -2.0, math.nan, math.inf):
+        assert decode(lib, d, params(softmax_scale=bad)) == -3
+        assert decode(lib, d, params(q_scale=bad)) == -3
+        assert decode(lib, d, params(k_scale=bad)) == -3
+        assert decode(lib, d, params(v_scale=bad)) == -3
+    assert decode(lib, d, params(), B=0) == 0                    # no sequences: no launch
+    assert decode(lib, d, params(), max_len=64 * 16 + 1) == -1   # table too short
+    assert decode(lib, d, params(), q=FAKE + 2) == -1
+    assert decode(lib, e4m3_desc(format=7), params()) == -2
+    # forced splits need a workspace: too small -> KVQ_ERR_WORKSPACE
+    p = params(num_splits=4)
+    need = lib.kvq_decode_workspace_bytes(ctypes.byref(d), 2, 1000, ctypes.byref(p))
+    assert need == 2 * 32 * 4 * (128 + 2) * 4
+    assert decode(lib, d, p, max_len=1000) == -4
+    assert decode(lib, d, p, max_len=1000, ws=FAKE, ws_bytes=need - 4) == -4
+    # one split needs none
+    assert lib.kvq_decode_workspace_bytes(ctypes.byref(d), 2, 1000, ctypes.byref(params(num_splits=1))) == 0
+
+
+def test_prefill_validation(lib):
+    d = e4m3_desc()
+    f = lib.kvq_paged_attn_prefill
+    p = params()
+    assert f(ctypes.byref(d), FAKE, FAKE, 10, 5, FAKE, 64, FAKE, 2, 100, ctypes.byref(params(num_q_heads=31)),
+             FAKE, None, 0, None) == -1
+    assert f(ctypes.byref(d), FAKE, FAKE, 0, 0, FAKE, 64, FAKE, 2, 100, ctypes.byref(p), FAKE, None, 0, None) == 0
+    assert f(ctypes.byref(d), FAKE, FAKE, 10, 200, FAKE, 64, FAKE, 2, 100, ctypes.byref(p), FAKE, None, 0,
+             None) == -1                                        # max_q_len > max_seq_len
+    nv = kvq.CacheDesc(2, 16, 1, 576, 64, FAKE, None)
+    assert f(ctypes.byref(nv), FAKE, FAKE, 10, 5, FAKE, 64, FAKE, 2, 100, ctypes.byref(params(num_q_heads=16)),
+             FAKE, None, 0, None) == -2
