@@ -1,0 +1,341 @@
+"""Benchmark of the quantized-KV-cache attention path on one MI355X.
+
+A step is one decode step of the batched-decode workload (batch 64, 8,192-token
+context, 32 query / 4 KV heads, head_dim 128, 16-token pages): quant-on-store
+of the 64 new tokens' K/V into the paged e4m3 cache, then fp8 paged decode
+attention over the full context (Q quantization, split-KV attention, combine).
+Scales come from amax calibration over the resident inputs before timing.
+
+``value`` is the step's algorithmic HBM bytes divided by the step time (GB/s).
+The JSON line also carries the roofline of the dominant kernel (decode attention,
+timed with HIP events on the launch stream), the other rows of the path measured
+in the same run (bulk store tokens/s, calibration, long-context decode, chunked
+prefill, NVFP4 record store and MLA decode), and the CPU oracle timed on a
+bounded sample as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-extras]
+       [--skip-cpu] [--only-decode] [--copy-probe]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+FP8_PEAK_TFLOPS = 5000.0        # dense fp8 MFMA
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--skip-extras", action="store_true", help="only the headline step")
+    ap.add_argument("--skip-cpu", action="store_true", help="no CPU oracle baseline")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+class EventTimer:
+    """Accumulates kernel time between HIP events recorded on one stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+def decode_bytes(B, Hq, Hkv, D, L):
+    """Algorithmic HBM bytes of one decode call: K and V codes of every attended
+    token, bf16 Q in and bf16 O out, block table and lengths."""
+    kv = B * L * Hkv * D * 2
+    return kv + B * Hq * D * 2 * 2 + B * ((L + 15) // 16) * 4 + B * 4
+
+
+def store_bytes(T, Hkv, D):
+    """bf16 K and V in, e4m3 K and V out, one int64 slot per token."""
+    return T * (Hkv * D * (2 * 2 + 2) + 8)
+
+
+TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "decode_e4m3_batched_decode.md")
+
+
+def traffic_record():
+    """HBM traffic per launch of the decode kernel from the committed rocprofv3
+    counter summary, or None when the kernel sources changed since the
+    counters were taken (their SHA-256 no longer matches)."""
+    import hashlib
+    try:
+        line = [l for l in open(TRAFFIC_PROFILE) if l.startswith("traffic_record: ")][0]
+        rec = json.loads(line[len("traffic_record: "):])
+        root = os.path.dirname(os.path.abspath(__file__))
+        h = hashlib.sha256()
+        for f in rec["kernel_sources"]:
+            h.update(open(os.path.join(root, f), "rb").read())
+        if h.hexdigest() != rec["kernel_sources_sha256"]:
+            return None
+        return int(rec["traffic_bytes_per_launch"])
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+
+
+def copy_probe(torch):
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "note": "one copy kernel reads and writes n bytes"}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs on a single MI355X "
+              "(no collectives or sharding); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(torch)
+        return
+    import fp4_quantized_paged_amd as kvq
+    from workloads import config_batched_decode
+
+    kvq.lib()   # fail loudly when the HIP library is missing
+    torch.cuda.set_device(0)
+    dev = "cuda"
+
+    # ---------------- headline: batched decode step ----------------
+    log("generating batched-decode inputs")
+    c = config_batched_decode()
+    B, Hq, Hkv, D, L = c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim, c.max_seq_len
+    k = c.k.to(dev)
+    v = c.v.to(dev)
+    q = c.q.to(dev)
+    slot = torch.from_numpy(c.slot_mapping).to(dev)
+    bt = torch.from_numpy(c.block_table).to(dev)
+    seq_lens = torch.from_numpy(c.seq_lens).to(dev)
+    _, ks = kvq.calibrate_amax(k)
+    _, qs = kvq.calibrate_amax(q)
+    scales = {"k": float(ks.item()), "q": float(qs.item()), "v": float(c.v_scale_override)}
+    # two cache copies (1 GiB together) alternate between steps so the 256 MB
+    # Infinity Cache cannot serve the KV reads of one step from the last
+    caches = [kvq.E4M3Cache(c.num_pages, Hkv, D) for _ in range(2)]
+    for cache in caches:
+        kvq.store(cache, k, v, slot, scales["k"], scales["v"])
+    new_idx = torch.from_numpy(np.cumsum(c.seq_lens) - 1).to(dev)   # current token of each seq
+    k_new = k[new_idx].contiguous()
+    v_new = v[new_idx].contiguous()
+    slot_new = slot[new_idx].contiguous()
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    ws_bytes = kvq.decode_workspace_bytes(caches[0], B, L, Hq)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    timer = EventTimer(torch)
+
+    def step(i, timed):
+        cache = caches[i % 2]
+        kvq.store(cache, k_new, v_new, slot_new, scales["k"], scales["v"])
+        s = timer.start() if timed else None
+        kvq.decode(cache, q, bt, seq_lens, L, c.softmax_scale, scales["q"], scales["k"],
+                   scales["v"], out=out, workspace=ws)
+        if timed:
+            timer.stop(s)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    log("timing %d steps" % args.steps)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    dec_bytes = decode_bytes(B, Hq, Hkv, D, L)
+    step_bytes = dec_bytes + store_bytes(B, Hkv, D)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_ms = timer.mean_ms()
+    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+    result = {
+        "metric": "fp8 paged-decode attention HBM GB/s & % of peak; KV store tokens/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "data": "synthetic (seeded; Q/K RMS-normed amax 20, V std 8 with 0.1% outliers in [448, 1272])",
+        "config": {"workload": "batched_decode", "batch": B, "context": L, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": D, "page_size": 16, "kv_format": "e4m3",
+                   "scales": scales, "step": "store 64 new tokens + decode attention"},
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_e4m3_kernel (batched decode)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_record(),
+                     "bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_ms * 1e3, 2)},
+    }
+    log("decode %.2f us, %.0f GB/s (%.1f%% of peak)" % (dec_ms * 1e3, achieved,
+                                                         100 * achieved / HBM_PEAK_GBPS))
+    del caches, k_new, v_new
+
+    if not args.skip_extras:
+        result["rows"] = extras(torch, kvq, c, k, v, q, slot, scales)
+    del k, v, q
+    torch.cuda.empty_cache()
+
+    if not args.skip_cpu:
+        result["cpu_baseline"] = cpu_baseline(c)
+    print(json.dumps(result), flush=True)
+
+
+def timed_mean(torch, fn, reps=10, warm=2):
+    for _ in range(warm):
+        fn()
+    t = EventTimer(torch)
+    for _ in range(reps):
+        s = t.start()
+        fn()
+        t.stop(s)
+    return t.mean_ms()
+
+
+def extras(torch, kvq, c, k, v, q, slot, scales):
+    """Other rows of the path, each timed with HIP events (mean of reps)."""
+    rows = {}
+    Hkv, D = c.num_kv_heads, c.head_dim
+    T = k.shape[0]
+    # bulk quant-on-store of all 524,288 tokens
+    cache = kvq.E4M3Cache(c.num_pages, Hkv, D)
+    ms = timed_mean(torch, lambda: kvq.store(cache, k, v, slot, scales["k"], scales["v"]))
+    sb = store_bytes(T, Hkv, D)
+    rows["store_bulk"] = {"tokens": T, "us": round(ms * 1e3, 2),
+                          "tokens_per_s": round(T / (ms * 1e-3), 1),
+                          "GB_s": round(sb / (ms * 1e-3) / 1e9, 1),
+                          "pct_of_peak": round(100 * sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+    # decode append: the 64 new tokens only
+    idx = torch.from_numpy(np.cumsum(c.seq_lens) - 1).to(k.device)
+    kn, vn, sn = k[idx].contiguous(), v[idx].contiguous(), slot[idx].contiguous()
+    ms = timed_mean(torch, lambda: kvq.store(cache, kn, vn, sn, scales["k"], scales["v"]), reps=20)
+    rows["store_append"] = {"tokens": int(kn.shape[0]), "us": round(ms * 1e3, 2)}
+    # calibration over K and V
+    amax = torch.zeros(1, device=k.device)
+    ms = timed_mean(torch, lambda: (kvq.calibrate_amax(k, amax=amax), kvq.calibrate_amax(v, amax=amax)))
+    cb = 2 * k.numel() * 2
+    rows["calibrate_kv"] = {"us": round(ms * 1e3, 2), "GB_s": round(cb / (ms * 1e-3) / 1e9, 1)}
+    del cache
+    torch.cuda.empty_cache()
+    rows.update(long_context_rows(torch, kvq))
+    return rows
+
+
+def long_context_rows(torch, kvq):
+    from workloads import config_long_context
+    out = {}
+    log("long-context decode")
+    c = config_long_context()
+    dev = "cuda"
+    k, v, q = c.k.to(dev), c.v.to(dev), c.q.to(dev)
+    slot = torch.from_numpy(c.slot_mapping).to(dev)
+    bt = torch.from_numpy(c.block_table).to(dev)
+    sl = torch.from_numpy(c.seq_lens).to(dev)
+    sc = {n: float(kvq.calibrate_amax(x)[1].item()) for n, x in (("k", k), ("v", v), ("q", q))}
+    caches = [kvq.E4M3Cache(c.num_pages, c.num_kv_heads, c.head_dim) for _ in range(2)]
+    for cache in caches:
+        kvq.store(cache, k, v, slot, sc["k"], sc["v"])
+    del k, v
+    B, Hq, Hkv, D, L = c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim, c.max_seq_len
+    for w in (0, 512):
+        it = [0]
+
+        def run():
+            cache = caches[it[0] % 2]
+            it[0] += 1
+            kvq.decode(cache, q, bt, sl, L, c.softmax_scale, sc["q"], sc["k"], sc["v"], window=w)
+        ms = timed_mean(torch, run, reps=10)
+        att = min(L, w) if w else L
+        by = decode_bytes(B, Hq, Hkv, D, att)
+        out["long_context" + ("_window512" if w else "")] = {
+            "batch": B, "context": L, "attended": att, "us": round(ms * 1e3, 2),
+            "GB_s": round(by / (ms * 1e-3) / 1e9, 1),
+            "pct_of_peak": round(100 * by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+    del caches
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(c):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    decode attention (page gather, Q quantization, fp64 attention) for 64
+    sequences, and quant-on-store of 2 sequences' tokens."""
+    from threadpoolctl import threadpool_info
+    from oracle.kvcache import new_cache, store_e4m3, calibrate_amax
+    from oracle.attention import paged_decode
+    log("cpu oracle baseline")
+    k = c.k.float().numpy()
+    v = c.v.float().numpy()
+    q = c.q.float().numpy()
+    _, sk = calibrate_amax(k)
+    _, sq = calibrate_amax(q)
+    sv = c.v_scale_override
+    L = c.max_seq_len
+    n_store = 2
+    tok = np.arange(n_store * L)
+    kc, vc = new_cache(c.num_pages, c.num_kv_heads, 16, c.head_dim)
+    t0 = time.perf_counter()
+    store_e4m3(kc, vc, k[tok], v[tok], c.slot_mapping[tok], sk, sv)
+    t_store = time.perf_counter() - t0
+    # decode: reuse the stored pages of the first sequences for every sampled
+    # sequence (same shapes and work per sequence)
+    bt = c.block_table.copy()
+    for b in range(c.batch):
+        bt[b] = c.block_table[b % n_store]
+    t0 = time.perf_counter()
+    paged_decode(q, kc, vc, bt, c.seq_lens, c.softmax_scale, sq, sk, sv)
+    t_dec = time.perf_counter() - t0
+    by = decode_bytes(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim, L)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(by / t_dec / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "decode attention of all 64 sequences x 8,192 tokens (%.1f s) and "
+                      "quant-on-store of %d sequences (%d tokens, %.1f s) of the batched-decode "
+                      "workload; numpy fp64" % (t_dec, n_store, len(tok), t_store),
+            "store_tokens_per_s": round(len(tok) / t_store, 1),
+            "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

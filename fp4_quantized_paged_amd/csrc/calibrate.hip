@@ -49,7 +49,12 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(AmaxLaunch a) {
       for (int u = 0; u < kRowUnroll; ++u) {
         const int64_t rr = r + u * nwaves;
         keep[u] = rr < a.rows && (a.slot == nullptr || a.slot[rr] >= 0);
-        x[u] = keep[u] ? *(const uint4 *)(a.x + rr * a.row_stride + (c << 3)) : make_uint4(0, 0, 0, 0);
+        if (keep[u]) {
+          const v4u w = __builtin_nontemporal_load((const v4u *)(a.x + rr * a.row_stride + (c << 3)));
+          x[u] = make_uint4(w.x, w.y, w.z, w.w);
+        } else {
+          x[u] = make_uint4(0, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int u = 0; u < kRowUnroll; ++u) m = absmax_u4(x[u], m);
@@ -76,7 +81,7 @@ __global__ void amax_finalize_kernel(const float *amax, float *scale) {
 hipError_t launch_amax(const AmaxLaunch &a, int num_cus, hipStream_t s) {
   if (a.rows > 0) {
     int64_t blocks = (a.rows + kAmaxWaves * kRowUnroll - 1) / (kAmaxWaves * kRowUnroll);
-    const int64_t cap = (int64_t)num_cus * 8;
+    const int64_t cap = (int64_t)num_cus * 16;
     if (blocks > cap) blocks = cap;
     hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, s, a);
     hipError_t e = hipGetLastError();

@@ -106,111 +106,118 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   const float qpos = (float)(L - 1);
 
   float m_run = -INFINITY;   // running max, log2 domain
-  float l_run = 0.0f;        // this lane's partial sum of p
+  float l_run = 0.0f;        // this lane's partial sum of 2^8 p
   v4f o[kTiles];
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const size_t kv_head_stride = (size_t)16 * D;               // bytes per head-page
   const size_t page_stride = (size_t)a.hkv * kv_head_stride;  // bytes per page
+  const size_t g_off = (size_t)g * kv_head_stride;
   const int32_t *bt = a.block_table + (size_t)b * a.bt_stride;
 
   for (int blk = blk_begin + wave; blk < blk_end; blk += W) {
     const int pbase = page_lo + blk * 8;
-    // pages this lane touches: K rows come from pages pbase + 2*(row/4) + {0,1},
-    // V columns (and this lane's output keys) from pages pbase + 2*grp + {0,1}
-    const int kp0 = pbase + 2 * (row >> 2);
+    // Pages this lane touches: K rows come from pages pbase + 2*(row/4) + {0,1},
+    // V columns (and this lane's output keys) from pages pbase + 2*grp + {0,1}.
+    // Pages past the sequence end are clamped to its last page: their keys are
+    // masked and their V bytes zeroed below, so every load stays unconditional.
+    const int kp0 = min(pbase + 2 * (row >> 2), page_hi - 1);
+    const int kp1 = min(pbase + 2 * (row >> 2) + 1, page_hi - 1);
     const int vp0 = pbase + 2 * grp;
-    const bool kv0 = kp0 < page_hi, kv1 = kp0 + 1 < page_hi;
-    const bool vv0 = vp0 < page_hi, vv1 = vp0 + 1 < page_hi;
-    const int kphys0 = kv0 ? bt[kp0] : 0;
-    const int kphys1 = kv1 ? bt[kp0 + 1] : 0;
-    const int vphys0 = vv0 ? bt[vp0] : 0;
-    const int vphys1 = vv1 ? bt[vp0 + 1] : 0;
+    const int kphys0 = bt[kp0];
+    const int kphys1 = bt[kp1];
+    const int vphys0 = bt[min(vp0, page_hi - 1)];
+    const int vphys1 = bt[min(vp0 + 1, page_hi - 1)];
+    const bool edge = (pbase * 16 < lo) || ((pbase + 8) * 16 > L);
 
-    // ---- K operands: MFMA j takes token 4*(j%4) + (row%4) of page (j<4 ? kp0 : kp0+1)
+    // ---- K operands: MFMA j takes token 4*(j%4) + (row%4) of page (j<4 ? kp0 : kp1)
+    const uint8_t *kb0 = a.kc + (size_t)kphys0 * page_stride + g_off + (row & 3) * D + grp * 32;
+    const uint8_t *kb1 = a.kc + (size_t)kphys1 * page_stride + g_off + (row & 3) * D + grp * 32;
     v8i kop[8];
-    const bool kload = (D == 128 || grp < 2);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const bool valid = (j < 4 ? kv0 : kv1) && kload;
-      const int phys = j < 4 ? kphys0 : kphys1;
-      const int tok = 4 * (j & 3) + (row & 3);
-      if (valid) {
-        const uint4 *src = (const uint4 *)(a.kc + (size_t)phys * page_stride + (size_t)g * kv_head_stride +
-                                           (size_t)tok * D + grp * 32);
-        const uint4 x0 = src[0], x1 = src[1];
+      if (D == 128 || grp < 2) {
+        const uint8_t *src = (j < 4 ? kb0 : kb1) + 4 * (j & 3) * D;
+        const v4u x0 = __builtin_nontemporal_load((const v4u *)src);
+        const v4u x1 = __builtin_nontemporal_load((const v4u *)(src + 16));
         kop[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
       } else {
         kop[j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
       }
     }
     // ---- V^T operands: tile t, dim 16t + row, 16 tokens of vp0 then of vp0+1
+    const uint8_t *vb0 = a.vc + (size_t)vphys0 * page_stride + g_off + row * 16;
+    const uint8_t *vb1 = a.vc + (size_t)vphys1 * page_stride + g_off + row * 16;
     v8i vop[kTiles];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-      const int dim = 16 * t + row;
-      uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-      if (vv0) x0 = *(const uint4 *)(a.vc + (size_t)vphys0 * page_stride + (size_t)g * kv_head_stride + (size_t)dim * 16);
-      if (vv1) x1 = *(const uint4 *)(a.vc + (size_t)vphys1 * page_stride + (size_t)g * kv_head_stride + (size_t)dim * 16);
+      const v4u x0 = __builtin_nontemporal_load((const v4u *)(vb0 + 256 * t));
+      const v4u x1 = __builtin_nontemporal_load((const v4u *)(vb1 + 256 * t));
       vop[t] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     }
 
-    // ---- S^T = K Q^T: lane holds keys (vp0 + j/4, token 4*(j%4) + i) of query row
+    // ---- S^T = K Q^T: lane holds keys (vp0 + j/4, token 4*(j%4) + i) of its query row
     v4f sacc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) sacc[j] = mfma_16x16x128_e4m3(kop[j], qop, v4f{0.f, 0.f, 0.f, 0.f});
 
-    // ---- scores (log2 domain), masking, block max
+    // ---- scores in the log2 domain: x = raw * fold (+ bias); masked keys -inf
     const int kpos0 = vp0 * 16;   // absolute position of this lane's first key
-    float x[8][4];
+    if (has_bias) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kpos = kpos0 + 16 * (j >> 2) + 4 * (j & 3) + i;
+          const float bias = round_bf16_finite(slope * ((float)kpos - qpos));
+          sacc[j][i] = fmaf(sacc[j][i], a.fold_log2, bias * kLog2e);
+        }
+    }
+    if (edge) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kpos = kpos0 + 16 * (j >> 2) + 4 * (j & 3) + i;
+          sacc[j][i] = (kpos >= lo && kpos < L) ? sacc[j][i] : -INFINITY;
+        }
+    }
     float bmax = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kpos = kpos0 + 16 * (j >> 2) + 4 * (j & 3) + i;
-        float s = sacc[j][i] * a.fold_log2;
-        if (has_bias) {
-          const float bias = round_bf16_finite(slope * ((float)kpos - qpos));
-          s = fmaf(bias, kLog2e, s);
-        }
-        s = (kpos >= lo && kpos < L) ? s : -INFINITY;
-        x[j][i] = s;
-        bmax = fmaxf(bmax, s);
-      }
-    }
+      for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, sacc[j][i]);
     bmax = wave_max_xor(bmax, 16);
     bmax = wave_max_xor(bmax, 32);
-    const float m_new = fmaxf(m_run, bmax);
+    // without bias the max was taken on raw scores (fold > 0 keeps the order)
+    const float scale = has_bias ? 1.0f : a.fold_log2;
+    const float m_new = fmaxf(m_run, bmax * scale);
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_new;
-
-    // ---- P = 2^8 p as two e4m3 terms
+    // P = 2^8 p (exponent offset 8), split into two e4m3 terms
+    const float off = 8.0f - m_use;
     v8i phi, plo;
     float psum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float p[4], h[4];
+      float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(x[j][i] - m_use);
+        p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[j][i], scale, off));
         psum += p[i];
-        p[i] *= 256.0f;
       }
       const uint32_t hi = cvt4_e4m3(p[0], p[1], p[2], p[3]);
       const v2f h01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
       const v2f h23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-      h[0] = h01.x; h[1] = h01.y; h[2] = h23.x; h[3] = h23.y;
       phi[j] = (int)hi;
-      plo[j] = (int)cvt4_e4m3(p[0] - h[0], p[1] - h[1], p[2] - h[2], p[3] - h[3]);
+      plo[j] = (int)cvt4_e4m3(p[0] - h01.x, p[1] - h01.y, p[2] - h23.x, p[3] - h23.y);
     }
     l_run = l_run * alpha + psum;
 
-    // ---- zero V bytes of tokens outside [lo, L) on partial pages (they may
-    // hold stale or NaN bytes, and 0 * NaN would poison the MFMA)
-    const bool edge = (pbase * 16 < lo) || ((pbase + 8) * 16 > L);
+    // ---- zero V bytes of tokens outside [lo, L) (stale, NaN or clamped pages:
+    // 0 * NaN would poison the MFMA)
     if (edge) {
       uint32_t m0[4], m1[4];
       page_byte_mask(vp0 * 16, lo, L, m0);
@@ -225,10 +232,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       }
     }
 
-    // ---- O^T = V^T P^T, rescaled by alpha first
+    // ---- O^T = V^T P^T, rescaled first when any row's max moved
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) o[t] *= alpha;
+    }
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-      o[t] *= alpha;
       o[t] = mfma_16x16x128_e4m3(vop[t], phi, o[t]);
       o[t] = mfma_16x16x128_e4m3(vop[t], plo, o[t]);
     }
@@ -292,11 +302,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int w = 0; w < W; ++w) den += __builtin_amdgcn_exp2f(s_m[w * 16 + r] - Mu) * s_l[w * 16 + r];
     const int h = g * group + qt * 16 + r;
     if (splits == 1) {
-      const float val = den > 0.0f ? (acc / den) * (a.v_scale * (1.0f / 256.0f)) : 0.0f;
+      const float val = den > 0.0f ? (acc / den) * a.v_scale : 0.0f;
       a.out[((size_t)b * a.hq + h) * D + dcol] = (uint16_t)f32_to_bf16_bits(val);
     } else {
       const size_t pi = ((size_t)b * a.hq + h) * splits + split;
-      a.part_o[pi * D + dcol] = acc * (1.0f / 256.0f);
+      a.part_o[pi * D + dcol] = acc;
       if (dcol == 0) {
         a.part_ml[2 * pi] = M;
         a.part_ml[2 * pi + 1] = den;
