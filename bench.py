@@ -259,7 +259,54 @@ def extras(torch, kvq, c, k, v, q, slot, scales):
     del cache
     torch.cuda.empty_cache()
     rows.update(long_context_rows(torch, kvq))
+    rows.update(prefill_rows(torch, kvq))
     return rows
+
+
+def prefill_flops(seq_lens, q_lens, Hq, D, window=0):
+    """QK^T and PV multiply-adds of causal chunked prefill, 2 flops each:
+    4 * D per attended (query row, head, key)."""
+    visits = 0
+    for L, lq in zip(seq_lens, q_lens):
+        pos = np.arange(L - lq, L, dtype=np.int64)
+        keys = pos + 1 if window <= 0 else np.minimum(pos + 1, window)
+        visits += int(keys.sum())
+    return 4 * D * Hq * visits
+
+
+def prefill_rows(torch, kvq):
+    from workloads import config_chunked_prefill
+    log("chunked prefill")
+    c = config_chunked_prefill()
+    dev = "cuda"
+    k, v, q = c.k.to(dev), c.v.to(dev), c.q.to(dev)
+    slot = torch.from_numpy(c.slot_mapping).to(dev)
+    sc = {n: float(kvq.calibrate_amax(x)[1].item()) for n, x in (("k", k), ("v", v), ("q", q))}
+    cache = kvq.E4M3Cache(c.num_pages, c.num_kv_heads, c.head_dim)
+    cached, new = [torch.from_numpy(i).to(dev) for i in c.store_batches]
+    kvq.store(cache, k[cached].contiguous(), v[cached].contiguous(), slot[cached], sc["k"], sc["v"])
+    kn, vn, sn = k[new].contiguous(), v[new].contiguous(), slot[new].contiguous()
+    ms_store = timed_mean(torch, lambda: kvq.store(cache, kn, vn, sn, sc["k"], sc["v"]), reps=10)
+    del k, v
+    bt = torch.from_numpy(c.block_table).to(dev)
+    sl = torch.from_numpy(c.seq_lens).to(dev)
+    cu = torch.from_numpy(c.cu_q_lens).to(dev)
+    slopes = torch.from_numpy(c.slopes).to(dev)
+    out = torch.empty_like(q)
+    ms = timed_mean(torch, lambda: kvq.prefill(cache, q, cu, c.max_q_len, bt, sl, c.max_seq_len,
+                                               c.softmax_scale, sc["q"], sc["k"], sc["v"],
+                                               slopes=slopes, out=out), reps=5)
+    fl = prefill_flops(c.seq_lens, c.q_lens, c.num_q_heads, c.head_dim)
+    tf = fl / (ms * 1e-3) / 1e12
+    T = int(kn.shape[0])
+    del cache
+    torch.cuda.empty_cache()
+    return {"chunked_prefill": {"batch": c.batch, "new_tokens": int(c.q_lens[0]),
+                                "context": c.max_seq_len, "us": round(ms * 1e3, 1),
+                                "TFLOP_s": round(tf, 1), "flops": fl,
+                                "pct_of_fp8_peak": round(100 * tf / FP8_PEAK_TFLOPS, 2)},
+            "store_prefill_new": {"tokens": T, "us": round(ms_store * 1e3, 2),
+                                  "tokens_per_s": round(T / (ms_store * 1e-3), 1)}}
 
 
 def long_context_rows(torch, kvq):

@@ -279,7 +279,7 @@ int kvq_paged_attn_prefill(const kvq_cache *cache, const void *q, const int32_t 
   (void)workspace_bytes;
   int st = check_cache(cache);
   if (st != KVQ_OK) return st;
-  if (cache->format != KVQ_FMT_E4M3) return KVQ_ERR_UNSUPPORTED;
+  if (cache->format != KVQ_FMT_E4M3 || cache->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
   st = check_params(cache, params);
   if (st != KVQ_OK) return st;
   if (num_seqs < 0 || max_seq_len < 0 || total_q < 0 || max_q_len < 0) return KVQ_ERR_INVALID_ARG;

@@ -3,6 +3,5 @@
 
 namespace kvq {
 hipError_t launch_store_nvfp4(const StoreNvfp4Launch &, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_prefill_e4m3(const PrefillE4M3Launch &, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_decode_mla(const DecodeMlaLaunch &, const MlaPlan &, hipStream_t) { return hipErrorNotSupported; }
 }  // namespace kvq
