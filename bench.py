@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true", help="no CPU oracle baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--only", choices=["prefill", "long_context"], default=None,
+                    help="run only this row (for profiling); prints its JSON")
     return ap.parse_args()
 
 
@@ -133,6 +135,10 @@ def main():
 
     kvq.lib()   # fail loudly when the HIP library is missing
     torch.cuda.set_device(0)
+    if args.only is not None:
+        fn = {"prefill": prefill_rows, "long_context": long_context_rows}[args.only]
+        print(json.dumps(fn(torch, kvq)), flush=True)
+        return
     dev = "cuda"
 
     # ---------------- headline: batched decode step ----------------

@@ -42,17 +42,41 @@ constexpr int kVBytes = kBlkKeys * kD;          // 16 KB of V^T per block
 constexpr int kBiasN = 160;                     // bias table entries per wave
 constexpr int kLoadChunks = (kKBytes + kVBytes) / 16 / (64 * kPW);  // 16-byte chunks per thread
 
-// Swizzle of the 16-byte column chunks of a K row in LDS: the 8 lanes that
-// read one row chunk together (rows kidx = 32*(m/4) + const + m%4) hit 8
-// different chunk slots, i.e. all 64 banks once.
-__device__ __forceinline__ int kswz(int kidx) { return (kidx & 3) | (((kidx >> 5) & 1) << 2); }
+// Swizzle of the 16-byte column chunks of a K row in LDS. The 16 lanes of one
+// lane group read chunk c of rows kidx = 32*(m/4) + const + m%4, m = 0..15;
+// with slot = c ^ kswz(kidx) they cover 16 distinct 16-byte bank groups of a
+// 256-byte span (64 banks) and any 8 consecutive lanes 8 distinct groups of a
+// 128-byte span, so a ds_read_b128 pass never repeats a bank.
+__device__ __forceinline__ int kswz(int kidx) {
+  return ((kidx & 3) | (((kidx >> 5) & 1) << 2)) ^ ((kidx >> 6) & 1);
+}
 
-struct PrefillSmem {
-  uint8_t k[kKBytes];           // [128 keys][8 chunks of 16 B], chunk c at slot c ^ kswz(key)
-  uint8_t v[kVBytes];           // [8 pages][128 dims][16 tokens]
+struct __align__(16) PrefillSmem {
+  uint4 k[kKBytes / 16];        // [128 keys][8 chunks of 16 B], chunk c at slot c ^ kswz(key)
+  uint4 v[2 * kVBytes / 16];    // bf16 V^T: [8 pages][2 halves][128 dims][8 tokens]
   float bias[kPW][kBiasN];      // per wave: bias * log2(e) by distance
 };
 
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ v8bf as_v8bf(uint4 x) { return __builtin_bit_cast(v8bf, x); }
+
+// Two e4m3 bytes of w (the low pair or the high pair) -> two bf16 in one
+// dword. Exact: an e4m3 value has at most 4 significant bits and its exponent
+// range fits bf16, so the fp32 value's upper half is the bf16 value.
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  const v2f f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHi);
+  return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const v2bf p = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+template <bool kBias>
 __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blocks) {
   __shared__ PrefillSmem sm;
@@ -106,12 +130,11 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
       }
     }
   }
-  const bool has_bias = a.slopes != nullptr;
-  const float slope = has_bias ? a.slopes[head] : 0.0f;
+  const float slope = kBias ? a.slopes[head] : 0.0f;
 
   float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.0f, 0.0f};
   v4f o[2][8];
+  v4f ol[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};   // row sums of P (ones tile)
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -152,7 +175,7 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
       if (tensor == 0) {
         const int kidx = pg * 16 + (off >> 7);       // key row within the block
         const int chunk = (off >> 4) & 7;
-        *(uint4 *)(sm.k + kidx * kD + ((chunk ^ kswz(kidx)) << 4)) = pre[c];
+        sm.k[kidx * 8 + (chunk ^ kswz(kidx))] = pre[c];
       } else {
         uint4 x = pre[c];
         if (edge) {
@@ -170,7 +193,12 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
           }
           x.x &= mk[0]; x.y &= mk[1]; x.z &= mk[2]; x.w &= mk[3];
         }
-        *(uint4 *)(sm.v + pg * 2048 + off) = x;
+        // tokens 0..7 -> half 0, 8..15 -> half 1, as bf16
+        const int dim = off >> 4;
+        sm.v[(pg * 2 + 0) * 128 + dim] = make_uint4(e4m3x2_to_bf16x2<false>(x.x), e4m3x2_to_bf16x2<true>(x.x),
+                                                     e4m3x2_to_bf16x2<false>(x.y), e4m3x2_to_bf16x2<true>(x.y));
+        sm.v[(pg * 2 + 1) * 128 + dim] = make_uint4(e4m3x2_to_bf16x2<false>(x.z), e4m3x2_to_bf16x2<true>(x.z),
+                                                     e4m3x2_to_bf16x2<false>(x.w), e4m3x2_to_bf16x2<true>(x.w));
       }
     }
   };
@@ -186,7 +214,7 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
 
     // ---- per-wave bias table for this block: entry e <-> distance
     // d = (P0 - j0) + e - 127, value bf16(slope * -d) * log2(e)
-    if (has_bias) {
+    if (kBias) {
       for (int e = lane; e < kBiasN; e += 64) {
         const float d = (float)(P0 - j0 + e - 127);
         sm.bias[wave][e] = round_bf16_finite(slope * -d) * kLog2e;
@@ -197,21 +225,23 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
     }
 
     const bool edge = (j0 + kBlkKeys - 1 > P0) || (a.window > 0 && j0 < khi - a.window);
+    // ---- S^T = K Q^T for both column blocks, sharing every K operand read.
+    // Lane (row, grp) gets keys kidx = 32*grp + 16*(j/4) + 4*(j%4) + i of
+    // query row cb*16 + row.
+    v4f s[2][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kidx = 32 * (row >> 2) + 16 * (j >> 2) + 4 * (j & 3) + (row & 3);
+      const int c0 = 2 * grp;
+      const uint4 x0 = sm.k[kidx * 8 + (c0 ^ kswz(kidx))];
+      const uint4 x1 = sm.k[kidx * 8 + ((c0 + 1) ^ kswz(kidx))];
+      const v8i kop = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      s[0][j] = mfma_16x16x128_e4m3(kop, qop[0], v4f{0.f, 0.f, 0.f, 0.f});
+      s[1][j] = mfma_16x16x128_e4m3(kop, qop[1], v4f{0.f, 0.f, 0.f, 0.f});
+    }
+    uint4 pk[2][4];     // P in bf16: pk[cb][kk] holds keys 8kk .. 8kk+7 of the lane group
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      v8i phi, plo;
-      // ---- S^T = K Q^T: lane (row, grp) gets keys
-      // kidx = 32*grp + 16*(j/4) + 4*(j%4) + i of query row (cb*16 + row)
-      v4f s[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kidx = 32 * (row >> 2) + 16 * (j >> 2) + 4 * (j & 3) + (row & 3);
-        const int c0 = 2 * grp;
-        const uint4 x0 = *(const uint4 *)(sm.k + kidx * kD + (((c0) ^ kswz(kidx)) << 4));
-        const uint4 x1 = *(const uint4 *)(sm.k + kidx * kD + (((c0 + 1) ^ kswz(kidx)) << 4));
-        const v8i kop = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        s[j] = mfma_16x16x128_e4m3(kop, qop[cb], v4f{0.f, 0.f, 0.f, 0.f});
-      }
       const int r = cb * 16 + row;
       // This lane's keys are j0 + 32*grp + c, c = 16*(j/4) + 4*(j%4) + i in
       // [0, 32). Bias entry r - kidx + 127 = tb_base + (31 - c) with
@@ -219,70 +249,75 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
       const float *tb = &sm.bias[wave][r - 32 * grp + 96];
       const int c_hi = P0 + r - j0 - 32 * grp;              // keys with c <= c_hi are causal
       const int c_lo = a.window > 0 ? c_hi - a.window : -1;  // and c > c_lo inside the window
+      if (kBias) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = 16 * (j >> 2) + 4 * (j & 3) + i;
-          float x = has_bias ? fmaf(s[j][i], fold, tb[31 - c]) : s[j][i];
-          if (edge) x = (c <= c_hi && c > c_lo) ? x : -INFINITY;
-          s[j][i] = x;
-        }
+          for (int i = 0; i < 4; ++i)
+            s[cb][j][i] = fmaf(s[cb][j][i], fold, tb[31 - (16 * (j >> 2) + 4 * (j & 3) + i)]);
+      }
+      if (edge) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = 16 * (j >> 2) + 4 * (j & 3) + i;
+            s[cb][j][i] = (c <= c_hi && c > c_lo) ? s[cb][j][i] : -INFINITY;
+          }
+      }
       float bmax = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, s[j][i]);
+        for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, s[cb][j][i]);
       bmax = wave_max_xor(bmax, 16);
       bmax = wave_max_xor(bmax, 32);
-      const float scale = has_bias ? 1.0f : fold;
+      const float scale = kBias ? 1.0f : fold;
       const float m_new = fmaxf(m_run[cb], bmax * scale);
       const float m_use = m_new == -INFINITY ? 0.0f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_use);
       m_run[cb] = m_new;
-      const float off = 8.0f - m_use;
-      float psum = 0.0f;
+      // P = 2^(x - m); pk[cb][kk] = keys 8kk .. 8kk+7 (j = 2kk, 2kk+1), the
+      // B-operand slice of PV step kk
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float pv[4];
+      for (int kk = 0; kk < 4; ++kk) {
+        float pv[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(fmaf(s[j][i], scale, off));
-          psum += pv[i];
-        }
-        const uint32_t hi = cvt4_e4m3(pv[0], pv[1], pv[2], pv[3]);
-        const v2f h01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-        const v2f h23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-        phi[j] = (int)hi;
-        plo[j] = (int)cvt4_e4m3(pv[0] - h01.x, pv[1] - h01.y, pv[2] - h23.x, pv[3] - h23.y);
+        for (int e = 0; e < 8; ++e)
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(s[cb][2 * kk + (e >> 2)][e & 3], scale, -m_use));
+        pk[cb][kk] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
       }
-      l_run[cb] = l_run[cb] * alpha + psum;
       if (__ballot(alpha != 1.0f)) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) o[cb][t] *= alpha;
+        ol[cb] *= alpha;
       }
-      // ---- O^T += V^T P^T: tile t covers dims 16t .. 16t+15
+    }
+    // ---- O^T += V^T P^T (bf16 MFMA, 32 keys per step) for both column
+    // blocks from one V^T operand read; tile t covers dims 16t .. 16t+15,
+    // step kk keys 8kk .. 8kk+7 of every lane group. A ones tile accumulates
+    // the row sums of the same rounded P.
+    const v8bf ones = as_v8bf(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const v8bf p0 = as_v8bf(pk[0][kk]), p1 = as_v8bf(pk[1][kk]);
+      const uint4 *vrow = sm.v + ((2 * grp + (kk >> 1)) * 2 + (kk & 1)) * 128 + row;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const int dim = 16 * t + row;
-        const uint4 x0 = *(const uint4 *)(sm.v + (2 * grp) * 2048 + dim * 16);
-        const uint4 x1 = *(const uint4 *)(sm.v + (2 * grp + 1) * 2048 + dim * 16);
-        const v8i vop = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        o[cb][t] = mfma_16x16x128_e4m3(vop, phi, o[cb][t]);
-        o[cb][t] = mfma_16x16x128_e4m3(vop, plo, o[cb][t]);
+        const v8bf va = as_v8bf(vrow[16 * t]);
+        o[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, p0, o[0][t], 0, 0, 0);
+        o[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, p1, o[1][t], 0, 0, 0);
       }
-      // keep the two column blocks' work apart: interleaving them doubles
-      // the live scores and operands
-      __builtin_amdgcn_sched_barrier(0);
+      ol[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, p0, ol[0], 0, 0, 0);
+      ol[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, p1, ol[1], 0, 0, 0);
     }
   }
 
   // ---- normalise and write bf16 rows: lane holds O[row][16t + 4*grp + i]
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    float l = l_run[cb];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = ol[cb][0];
     const int r = cb * 16 + row;
     if (!head_ok || r >= ntok) continue;
     const float f = l > 0.0f ? a.v_scale / l : 0.0f;
@@ -306,8 +341,12 @@ hipError_t launch_prefill_e4m3(const PrefillE4M3Launch &a, hipStream_t s) {
   const int tiles = (a.max_q_len + kTileTok - 1) / kTileTok;
   if (tiles == 0) return hipSuccess;
   const size_t grid = (size_t)8 * ((units + 7) / 8) * tiles;
-  hipLaunchKernelGGL(prefill_e4m3_kernel, dim3((unsigned)grid), dim3(64 * kPW), 0, s, a, tiles, units,
-                     head_blocks);
+  if (a.slopes != nullptr)
+    hipLaunchKernelGGL(prefill_e4m3_kernel<true>, dim3((unsigned)grid), dim3(64 * kPW), 0, s, a, tiles, units,
+                       head_blocks);
+  else
+    hipLaunchKernelGGL(prefill_e4m3_kernel<false>, dim3((unsigned)grid), dim3(64 * kPW), 0, s, a, tiles, units,
+                       head_blocks);
   return hipGetLastError();
 }
 
