@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true", help="no CPU oracle baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a 1 GiB device copy (HBM counter calibration)")
-    ap.add_argument("--only", choices=["prefill", "long_context"], default=None,
+    ap.add_argument("--only", choices=["prefill", "long_context", "nvfp4"], default=None,
                     help="run only this row (for profiling); prints its JSON")
     return ap.parse_args()
 
@@ -136,7 +136,7 @@ def main():
     kvq.lib()   # fail loudly when the HIP library is missing
     torch.cuda.set_device(0)
     if args.only is not None:
-        fn = {"prefill": prefill_rows, "long_context": long_context_rows}[args.only]
+        fn = {"prefill": prefill_rows, "long_context": long_context_rows, "nvfp4": nvfp4_rows}[args.only]
         print(json.dumps(fn(torch, kvq)), flush=True)
         return
     dev = "cuda"
@@ -266,7 +266,50 @@ def extras(torch, kvq, c, k, v, q, slot, scales):
     torch.cuda.empty_cache()
     rows.update(long_context_rows(torch, kvq))
     rows.update(prefill_rows(torch, kvq))
+    rows.update(nvfp4_rows(torch, kvq))
     return rows
+
+
+def nvfp4_rows(torch, kvq):
+    """NVFP4 368-byte records: bulk store of 524,288 tokens and MLA decode
+    (batch 32 x 16,384 tokens, 16 heads). Algorithmic bytes: bf16 token in
+    (1,152 B) + record out (368 B) + slot (8 B) per stored token; records +
+    bf16 Q + bf16 O + block table + lengths per decode call."""
+    from workloads import config_nvfp4_mla
+    log("nvfp4 mla")
+    c = config_nvfp4_mla(layer=0)
+    dev = "cuda"
+    kv = c.kv.to(dev)
+    slot = torch.from_numpy(c.slot_mapping).to(dev)
+    caches = [kvq.Nvfp4Cache(c.num_pages) for _ in range(2)]
+    ms_store = timed_mean(torch, lambda: kvq.store(caches[0], kv, None, slot, c.rope_scale), reps=5)
+    kvq.store(caches[1], kv, None, slot, c.rope_scale)
+    T = int(kv.shape[0])
+    del kv
+    q = c.q.to(dev)
+    bt = torch.from_numpy(c.block_table).to(dev)
+    sl = torch.from_numpy(c.seq_lens).to(dev)
+    out = torch.empty((c.batch, c.num_q_heads, 512), dtype=torch.bfloat16, device=dev)
+    it = [0]
+
+    def run():
+        cache = caches[it[0] % 2]     # 2 x 193 MB alternate: more than the Infinity Cache
+        it[0] += 1
+        kvq.decode(cache, q, bt, sl, c.max_seq_len, c.softmax_scale, k_scale=c.rope_scale, out=out)
+    ms = timed_mean(torch, run, reps=10)
+    L = c.max_seq_len
+    by = c.batch * (L * 368 + c.num_q_heads * (576 + 512) * 2 + ((L + 15) // 16) * 4 + 4)
+    sb = T * (576 * 2 + 368 + 8)
+    del caches
+    torch.cuda.empty_cache()
+    return {"nvfp4_mla_decode": {"batch": c.batch, "context": L, "heads": c.num_q_heads,
+                                 "us": round(ms * 1e3, 2), "GB_s": round(by / (ms * 1e-3) / 1e9, 1),
+                                 "pct_of_peak": round(100 * by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                                 "bytes": by},
+            "nvfp4_store": {"tokens": T, "us": round(ms_store * 1e3, 2),
+                            "tokens_per_s": round(T / (ms_store * 1e-3), 1),
+                            "GB_s": round(sb / (ms_store * 1e-3) / 1e9, 1),
+                            "pct_of_peak": round(100 * sb / (ms_store * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}}
 
 
 def prefill_flops(seq_lens, q_lens, Hq, D, window=0):

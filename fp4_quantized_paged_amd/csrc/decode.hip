@@ -28,6 +28,7 @@
 //  * W waves merge through LDS; with one split the workgroup writes bf16 out
 //    directly, otherwise (m, l, o) partials go to the workspace and the
 //    combine kernel merges them.
+#include "kvq_combine.h"
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -315,27 +316,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   }
 }
 
-// Merge split partials: out = v_scale * sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const float *part_o, const float *part_ml,
-                                                            uint16_t *out, int splits, float v_scale) {
-  const int bh = blockIdx.x;          // b * hq + h
-  const int dcol = threadIdx.x;
-  const float *ml = part_ml + (size_t)bh * splits * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[2 * s]);
-  const float Mu = M == -INFINITY ? 0.0f : M;
-  float acc = 0.0f, den = 0.0f;
-  const float *po = part_o + (size_t)bh * splits * D + dcol;
-  for (int s = 0; s < splits; ++s) {
-    const float f = __builtin_amdgcn_exp2f(ml[2 * s] - Mu);
-    acc += f * po[(size_t)s * D];
-    den += f * ml[2 * s + 1];
-  }
-  const float val = den > 0.0f ? (acc / den) * v_scale : 0.0f;
-  out[(size_t)bh * D + dcol] = (uint16_t)f32_to_bf16_bits(val);
-}
-
 template <int D, int W>
 hipError_t launch_decode_t(const DecodeE4M3Launch &a, const DecodePlan &p, hipStream_t s) {
   const size_t grid = (size_t)a.batch * a.hkv * p.qtiles * p.splits;
@@ -344,7 +324,7 @@ hipError_t launch_decode_t(const DecodeE4M3Launch &a, const DecodePlan &p, hipSt
                      p.splits, p.blocks_per_split, p.qtiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)((size_t)a.batch * a.hq)), dim3(D), 0, s,
+  hipLaunchKernelGGL((split_combine_kernel<D>), dim3((unsigned)((size_t)a.batch * a.hq)), dim3(D), 0, s,
                      a.part_o, a.part_ml, a.out, p.splits, a.v_scale);
   return hipGetLastError();
 }

@@ -100,7 +100,7 @@ kvq::DecodePlan plan_decode(const kvq_cache *c, int32_t num_seqs, int32_t max_se
 kvq::MlaPlan plan_mla(int32_t num_seqs, int32_t max_seq_len, const kvq_attn_params *p) {
   kvq::MlaPlan pl{};
   const int64_t pages = max_seq_len > 0 ? (static_cast<int64_t>(max_seq_len) + 15) / 16 : 1;
-  const int64_t target = static_cast<int64_t>(current_cu_count()) * 4;
+  const int64_t target = static_cast<int64_t>(current_cu_count()) * 2;   // workgroups of 4 waves
   int64_t splits = p->num_splits > 0 ? p->num_splits : (target + num_seqs - 1) / (num_seqs > 0 ? num_seqs : 1);
   // at least 4 pages (64 keys) per split
   const int64_t max_splits = (pages + 3) / 4;
@@ -249,6 +249,7 @@ int kvq_paged_attn_decode(const kvq_cache *cache, const void *q, const int32_t *
     a.v_scale = params->v_scale;
     return hip_status(kvq::launch_decode_e4m3(a, pl, reinterpret_cast<hipStream_t>(stream)));
   }
+  if (params->num_q_heads != 16) return KVQ_ERR_UNSUPPORTED;
   const kvq::MlaPlan pl = plan_mla(num_seqs, max_seq_len, params);
   if (pl.workspace > 0 && (workspace == nullptr || workspace_bytes < pl.workspace)) return KVQ_ERR_WORKSPACE;
   if (pl.workspace > 0 && !aligned16(workspace)) return KVQ_ERR_INVALID_ARG;

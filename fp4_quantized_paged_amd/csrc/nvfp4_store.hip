@@ -1,0 +1,142 @@
+// NVFP4 368-byte MLA latent record store.
+//
+// local-inference-lab/vllm PR 189, "mla: wire dynamic per-token NVFP4 scaling
+// and cache ABI" (commit message, "Why"): the 512-dim latent is stored as e2m1
+// values with one E4M3 scale per group, next to an fp8 RoPE part, and the
+// writer derives a per-token second-level scale that it stores inside the
+// record at bytes [292, 296) of existing padding; the record stays 368 bytes.
+//
+// Per token (all arithmetic fp32, divisions correctly rounded):
+//   s2 = amax(latent) / 2688                  (2688 = e2m1 max 6 * e4m3 max 448)
+//   group g (16 elements): sg = e4m3_RNE(min(ag / fp32(6 * s2), 448))
+//   dg = fp32(e4m3(sg) * s2); codes = e2m1_RNE(clip(x * fp32(1 / dg), -6, 6)),
+//   or +0 codes when dg == 0 (also for an all-zero token, where s2 = 0)
+//   RoPE: the e4m3 store quantizer with the rope scale
+// Record: [0,256) values, element 2i in the low nibble of byte i; [256,288)
+// group-scale codes; [288,292) zero; [292,296) s2 (little endian);
+// [296,304) zero; [304,368) RoPE codes.
+//
+// One 32-lane half of a wave handles one token, one lane per 16-element group
+// (plus two RoPE elements per lane). The record is assembled in LDS and
+// leaves as 23 16-byte stores; the 16 records of a page are contiguous.
+#include "kvq_device.h"
+#include "kvq_launch.h"
+
+#pragma clang fp contract(off)
+
+namespace kvq {
+
+namespace {
+
+constexpr int kRec = 368;
+constexpr int kTokensPerBlock = 8;        // 4 waves x 2 tokens
+constexpr int kThreads = 256;
+
+// e2m1 code (0..7) of a magnitude already clipped to [0, 6], round to nearest
+// even code: the grid is evenly spaced inside each binade, so rint on the
+// scaled magnitude (ties to even) is the even code.
+__device__ __forceinline__ uint32_t e2m1_code(float a) {
+  const float c0 = __builtin_rintf(a * 2.0f);          // 0, .5, 1, 1.5, 2 -> 0..4
+  const float c1 = __builtin_rintf(a) + 2.0f;          // 2, 3, 4 -> 4..6
+  const float c2 = __builtin_rintf(a * 0.5f) + 4.0f;   // 4, 6 -> 6, 7
+  const float c = a < 2.0f ? c0 : (a < 4.0f ? c1 : c2);
+  return (uint32_t)c;
+}
+
+__device__ __forceinline__ uint32_t e2m1_encode(float y) {
+  const float a = fminf(fabsf(y), 6.0f);
+  return e2m1_code(a) | ((__float_as_uint(y) >> 28) & 8u);   // sign bit kept
+}
+
+__global__ __launch_bounds__(kThreads) void store_nvfp4_kernel(StoreNvfp4Launch a) {
+  __shared__ __align__(16) uint8_t rec[kTokensPerBlock][kRec];
+  const int tid = threadIdx.x;
+  const int half = tid >> 5;                 // token within the block
+  const int g = tid & 31;                    // latent group / RoPE pair
+  const int64_t t = (int64_t)blockIdx.x * kTokensPerBlock + half;
+  const bool live = t < a.num_tokens;
+  const int64_t slot = live ? a.slot[t] : -1;
+
+  // ---- load this lane's 16 latent elements and 2 RoPE elements
+  uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
+  uint32_t rp = 0;
+  if (slot >= 0) {
+    const uint16_t *src = a.x + t * a.stride;
+    const v4u w0 = __builtin_nontemporal_load((const v4u *)(src + 16 * g));
+    const v4u w1 = __builtin_nontemporal_load((const v4u *)(src + 16 * g + 8));
+    x0 = make_uint4(w0.x, w0.y, w0.z, w0.w);
+    x1 = make_uint4(w1.x, w1.y, w1.z, w1.w);
+    rp = *(const uint32_t *)(src + 512 + 2 * g);
+  }
+  const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+
+  // ---- group amax (|bf16| orders like its bits), token amax over 32 lanes
+  uint32_t ag_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ag_bits = max(ag_bits, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  uint32_t am_bits = ag_bits;
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) am_bits = max(am_bits, (uint32_t)__shfl_xor((int)am_bits, off, 32));
+  const float ag = __uint_as_float(ag_bits << 16);
+  const float amax = __uint_as_float(am_bits << 16);
+
+  // ---- two-level scales
+  const float s2 = amax / 2688.0f;
+  const float d = 6.0f * s2;
+  float ratio = amax > 0.0f ? ag / d : 0.0f;
+  ratio = fminf(ratio, kE4M3Max);
+  const uint32_t sg = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ratio, 0.0f, 0, false) & 0xFFu;
+  const v2f sgpair = __builtin_amdgcn_cvt_pk_f32_fp8((int)sg, false);
+  const float sgv = sgpair.x;
+  const float dg = sgv * s2;
+  const float r = dg != 0.0f ? 1.0f / dg : 0.0f;
+
+  // ---- e2m1 codes, two per byte (element 2i low nibble)
+  uint32_t packed[2] = {0u, 0u};
+  if (dg != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t lo = e2m1_encode(bf16lo(w[i]) * r);
+      const uint32_t hi = e2m1_encode(bf16hi(w[i]) * r);
+      packed[i >> 2] |= (lo | (hi << 4)) << (8 * (i & 3));
+    }
+  }
+  // ---- RoPE pair through the e4m3 store quantizer
+  const uint32_t rope = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(bf16lo(rp) * a.rope_inv),
+                                                                  sat448(bf16hi(rp) * a.rope_inv), 0, false) &
+                        0xFFFFu;
+
+  // ---- assemble the record in LDS
+  uint8_t *R = rec[half];
+  *(uint2 *)(R + 8 * g) = make_uint2(packed[0], packed[1]);
+  R[256 + g] = (uint8_t)sg;
+  *(uint16_t *)(R + 304 + 2 * g) = (uint16_t)rope;
+  if (g == 0) {
+    *(uint32_t *)(R + 288) = 0u;
+    *(float *)(R + 292) = s2;
+    *(uint2 *)(R + 296) = make_uint2(0u, 0u);
+  }
+  __syncthreads();
+
+  // ---- 23 16-byte stores per record
+  for (int c = tid; c < kTokensPerBlock * (kRec / 16); c += kThreads) {
+    const int tok = c / (kRec / 16);
+    const int part = c - tok * (kRec / 16);
+    const int64_t tt = (int64_t)blockIdx.x * kTokensPerBlock + tok;
+    if (tt >= a.num_tokens) continue;
+    const int64_t s = a.slot[tt];
+    if (s < 0) continue;
+    const v4u v = *(const v4u *)(rec[tok] + 16 * part);
+    __builtin_nontemporal_store(v, (v4u *)(a.records + (size_t)s * kRec + 16 * part));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_store_nvfp4(const StoreNvfp4Launch &a, hipStream_t s) {
+  const int64_t blocks = (a.num_tokens + kTokensPerBlock - 1) / kTokensPerBlock;
+  hipLaunchKernelGGL(store_nvfp4_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,119 @@
+"""GPU parity of the NVFP4 368-byte record store (bit-exact) and of the MLA
+decode over those records (within tolerance) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_quantized_paged_amd as kvq
+from oracle.codecs import bf16_round
+from oracle.nvfp4 import new_pool, store_records, mla_decode
+from workloads import bf16, make_mla_case, config_nvfp4_mla
+from workloads.gen import mla_layer_stds
+from parity import check_attention
+
+pytestmark = pytest.mark.gpu
+
+
+def special_tokens():
+    """Edge tokens: all zero, an exact two-level grid token (amax 168), a
+    token with an all-zero group, tiny magnitudes, huge magnitudes."""
+    rng = np.random.default_rng(17)
+    toks = []
+    toks.append(np.zeros(576, np.float32))
+    t = np.zeros(576, np.float32)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    t[0:16] = np.tile(grid, 2) * 28.0
+    t[0] = 168.0
+    t[16:32] = np.tile(grid, 2) * 0.125
+    t[512:] = rng.standard_normal(64).astype(np.float32)
+    toks.append(t)
+    t = rng.standard_normal(576).astype(np.float32)
+    t[32:48] = 0.0
+    toks.append(t)
+    toks.append(rng.standard_normal(576).astype(np.float32) * 1e-30)
+    toks.append(rng.standard_normal(576).astype(np.float32) * 1e30)
+    t = rng.standard_normal(576).astype(np.float32)
+    t[5] = -1000.0       # one dominant element: most group scales tiny
+    toks.append(t)
+    return bf16_round(np.stack(toks))
+
+
+@pytest.mark.parametrize("rope_scale", [1.0, 0.37])
+def test_store_records_bit_exact(rope_scale):
+    rng = np.random.default_rng(3)
+    parts = [special_tokens()]
+    for std in mla_layer_stds() + [1e-3, 30.0]:
+        parts.append(bf16_round((rng.standard_normal((40, 576)) * std).astype(np.float32)))
+    x = np.concatenate(parts)
+    T = x.shape[0]
+    num_pages = (T + 15) // 16 + 3
+    slot = rng.permutation(num_pages * 16)[:T].astype(np.int64)
+    slot[::7] = -1
+    cache = kvq.Nvfp4Cache(num_pages)
+    kvq.store(cache, bf16(x).cuda(), None, torch.from_numpy(slot).cuda(), rope_scale)
+    torch.cuda.synchronize()
+    pool = new_pool(num_pages)
+    store_records(pool, x, slot, rope_scale)
+    got = cache.records.cpu().numpy()
+    bad = np.argwhere(got != pool)
+    assert bad.size == 0, bad[:10]
+
+
+def test_store_full_size_sampled():
+    """All 524,288 tokens of the layer with std 0.05; four sequences compared."""
+    c = config_nvfp4_mla(layer=0)
+    cache = kvq.Nvfp4Cache(c.num_pages)
+    kv = c.kv.cuda()
+    kvq.store(cache, kv, None, torch.from_numpy(c.slot_mapping).cuda(), c.rope_scale)
+    torch.cuda.synchronize()
+    starts = np.concatenate([[0], np.cumsum(c.seq_lens)])
+    tok = np.concatenate([np.arange(starts[b], starts[b + 1]) for b in (0, 9, 20, 31)])
+    pool = new_pool(c.num_pages)
+    store_records(pool, c.kv.float().numpy()[tok], c.slot_mapping[tok], c.rope_scale)
+    pages = np.unique(c.slot_mapping[tok] // 16)
+    got = cache.records[torch.from_numpy(pages).cuda()].cpu().numpy()
+    assert np.array_equal(got, pool[pages])
+
+
+def run_mla(c, seqs=None, **kw):
+    cache = kvq.Nvfp4Cache(c.num_pages)
+    kvq.store(cache, c.kv.cuda(), None, torch.from_numpy(c.slot_mapping).cuda(), c.rope_scale)
+    out = kvq.decode(cache, c.q.cuda(), torch.from_numpy(c.block_table).cuda(),
+                     torch.from_numpy(c.seq_lens).cuda(), c.max_seq_len, c.softmax_scale,
+                     k_scale=c.rope_scale, **kw)
+    torch.cuda.synchronize()
+    starts = np.concatenate([[0], np.cumsum(c.seq_lens)])
+    sel = range(c.batch) if seqs is None else seqs
+    tok = np.concatenate([np.arange(starts[b], starts[b + 1]) for b in sel])
+    pool = new_pool(c.num_pages)
+    store_records(pool, c.kv.float().numpy()[tok], c.slot_mapping[tok], c.rope_scale)
+    ref = mla_decode(c.q.float().numpy(), pool, c.block_table, c.seq_lens, c.softmax_scale,
+                     c.rope_scale, seqs=seqs)
+    if seqs is not None:
+        return out[torch.tensor(seqs)], ref[seqs]
+    return out, ref
+
+
+@pytest.mark.parametrize("std", [0.05, 1.0, 4.0])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_mla_decode_shapes(std, splits):
+    c = make_mla_case("mla", 50 + int(std * 10), [1, 15, 16, 17, 300, 1000], layer_std=std,
+                      rope_scale=0.8)
+    out, ref = run_mla(c, num_splits=splits)
+    print(check_attention(out, ref, "mla std %g splits %d" % (std, splits)))
+
+
+def test_mla_decode_zero_length_and_poison():
+    c = make_mla_case("mla0", 61, [0, 33, 5], layer_std=1.0, spare_frac=2.0)
+    out, ref = run_mla(c)
+    assert torch.all(out[0] == 0)
+    assert torch.all(torch.isfinite(out.float()))
+    check_attention(out, ref, "mla zero/poison")
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_mla_decode_full_size_sampled(layer):
+    """Batch 32 x 16,384 tokens; four sequences compared with the oracle."""
+    c = config_nvfp4_mla(layer=layer)
+    out, ref = run_mla(c, seqs=[0, 7, 19, 31])
+    print(check_attention(out, ref, "nvfp4 mla layer %d" % layer))
