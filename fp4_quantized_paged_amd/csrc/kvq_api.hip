@@ -100,11 +100,13 @@ kvq::DecodePlan plan_decode(const kvq_cache *c, int32_t num_seqs, int32_t max_se
 kvq::MlaPlan plan_mla(int32_t num_seqs, int32_t max_seq_len, const kvq_attn_params *p) {
   kvq::MlaPlan pl{};
   const int64_t pages = max_seq_len > 0 ? (static_cast<int64_t>(max_seq_len) + 15) / 16 : 1;
-  const int64_t target = static_cast<int64_t>(current_cu_count()) * 2;   // workgroups of 4 waves
+  const int64_t target = static_cast<int64_t>(current_cu_count());   // one 12-wave workgroup per CU
   int64_t splits = p->num_splits > 0 ? p->num_splits : (target + num_seqs - 1) / (num_seqs > 0 ? num_seqs : 1);
-  // at least 4 pages (64 keys) per split
+  // at least 4 pages (64 keys) per split, at most 512 (the kernel stages a
+  // split's block-table slice in LDS)
   const int64_t max_splits = (pages + 3) / 4;
   if (splits > max_splits) splits = max_splits;
+  if (splits < (pages + 511) / 512) splits = (pages + 511) / 512;
   if (splits < 1) splits = 1;
   pl.pages_per_split = static_cast<int>((pages + splits - 1) / splits);
   pl.splits = static_cast<int>((pages + pl.pages_per_split - 1) / pl.pages_per_split);
@@ -112,7 +114,7 @@ kvq::MlaPlan plan_mla(int32_t num_seqs, int32_t max_seq_len, const kvq_attn_para
     pl.workspace = 0;
   } else {
     const size_t rows = static_cast<size_t>(num_seqs) * p->num_q_heads * pl.splits;
-    pl.workspace = rows * (512 + 2) * sizeof(float);
+    pl.workspace = rows * (512 + 4) * sizeof(float);   // O partial, then (M, den, E, pad)
   }
   return pl;
 }

@@ -85,7 +85,7 @@ struct DecodeMlaLaunch {
   const int32_t *seq_lens;
   uint16_t *out;               // [B][Hq][512]
   float *part_o;               // [B][Hq][S][512]
-  float *part_ml;              // [B][Hq][S][2]
+  float *part_ml;              // [B][Hq][S][4]: M, den, E, pad
   int batch, hq;
   float scale_log2;            // softmax_scale * log2(e)
   float rope_scale;

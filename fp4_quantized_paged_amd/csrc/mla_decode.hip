@@ -5,28 +5,39 @@
 // and cache ABI" (commit message, "Why"): readers take the per-token outer
 // scale from bytes [292, 296) of each record instead of a per-layer launch
 // scalar. Per key j:
-//   latent_j = e2m1(v) * e4m3(sg) * s2_j        (the group product is exact in bf16)
+//   latent_j = e2m1(v) * e4m3(sg) * s2_j
 //   K_j = [latent_j ; e4m3(rope_j) * rope_scale],  V_j = latent_j
 //   s_j = softmax_scale * (s2_j * (q_lat . Kt_j) + rope_scale * (q_rope . r_j))
 // with Kt_j = e2m1 * e4m3(sg); out = sum_j p_j s2_j Kt_j / sum_j p_j.
 //
-// Kernel design (gfx950, wave64, 8 waves per workgroup, one workgroup per
-// (sequence, split), waves take interleaved 16-token pages; Q sits in LDS):
-//  * QK^T on v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 latent dims, B = the
-//    16 query heads. Lane (key l%16, group g) dequantizes dims 128g + 8c..+8
-//    for step c straight from its record (hardware fp4 -> fp32 conversion at
-//    unit scale, then the fp32 group scale, packed to bf16) and feeds the MFMA
-//    from registers; the RoPE part takes two more MFMAs with its own
-//    accumulator;
-//  * the same bf16 values go to LDS row-major ([key][dim], rows padded to
-//    avoid bank conflicts); PV (v_mfma_f32_16x16x16_bf16, A = V^T) reads them
-//    back with ds_read_b64_tr_b16, whose 16-lane transpose turns four row
-//    segments into one dim x 4 keys operand: no transposed copy is written;
-//  * the S^T output lane (keys 4g..4g+3 of head l%16) is already the B
-//    operand of the 16x16x16 PV step; s2 is folded into P;
-//  * waves merge through LDS; with one split the workgroup writes bf16, else
-//    partials go to the workspace for the shared split combine.
-#include "kvq_combine.h"
+// Kernel design (gfx950, wave64, one workgroup of 4 wave pairs per
+// (sequence, split); pairs take interleaved 16-key pages):
+//  * the two waves of a pair split the 512 latent dims (256 each) and the 64
+//    RoPE dims (32 each). Every product e2m1 * e4m3 is exact in fp16, so the
+//    latent is dequantized by the hardware fp4 -> fp16 conversion and one
+//    packed fp16 multiply per two values. Q is held in registers as fp16,
+//    pre-scaled per head by a power of two that puts its largest element in
+//    [2^13, 2^14) (exact for all but elements 2^-31 below the head maximum);
+//  * QK^T on v_mfma_f32_16x16x32_f16 (A = 16 keys x 32 dims from registers,
+//    B = the 16 heads). The two half-dot-products meet through LDS (one
+//    workgroup barrier per page); both waves then run the same softmax on
+//    identical scores;
+//  * the dequantized rows also go to LDS (chunk-major, bank-conflict free,
+//    two buffers per wave) and PV (v_mfma_f32_16x16x16_f16, A = V^T) reads
+//    them back with ds_read_b64_tr_b16, whose 16-lane transpose turns four
+//    row segments into one dim x 4 keys operand. The PV of page k-1 is
+//    interleaved with the dequant and QK^T of page k, so the vector ALU and
+//    the matrix cores work at the same time;
+//  * each wave keeps four pages of record bytes in flight;
+//  * P enters PV in fp16. Per pair, Gs is the largest exponent of the outer
+//    scales seen so far; the keys' scales enter P as s2 * 2^-Gs < 1. Per head,
+//    the running max m is integer-valued and raised only when a score passes
+//    it by more than 8 (log2 units), so 2^(x - m) <= 2^8 and P stays far
+//    below the fp16 limit. The accumulator holds
+//    O_acc = 2^-Gs sum_j 2^(x_j - m) s2_j Kt_j; it is rescaled (by powers of
+//    two) only when m or Gs moves;
+//  * pairs merge through LDS; with one split the workgroup writes bf16, else
+//    (O, m, l, m + Gs) partials go to the workspace for the split combine.
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -34,58 +45,106 @@ namespace kvq {
 
 namespace {
 
-constexpr int kMW = 8;                // waves per workgroup (one workgroup per CU)
+constexpr int kPairs = 4;
+constexpr int kWaves = 2 * kPairs;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRec = 368;
 constexpr int kLat = 512;
-constexpr int kRowB = 2 * kLat + 32;  // LDS bytes per key row (pad: conflict-free transpose reads)
+constexpr int kHalf = 256;            // latent dims per wave
 constexpr int kHeads = 16;
-constexpr int kQRowB = 2 * (kLat + 64) + 16;   // LDS bytes per query head (pad: conflict-free)
+constexpr int kKtBytes = 16 * kHalf * 2;          // fp16 K rows of one page, one wave
+constexpr int kStageRowU4 = (kLat + 64) / 8 + 1;  // bf16 Q staging row, uint4 units
+constexpr float kTau = 8.0f;                      // lazy-max slack, log2 units
+constexpr int kGUnset = -(1 << 20);               // Gs before any nonzero outer scale
+constexpr int kSlabRow = kHalf + 4;               // merge slab row (floats, padded)
+constexpr int kMaxSplitPages = 512;               // pages of one split (the planner's cap)
+constexpr int kBufs = 4;                          // pages of record bytes in flight per wave
 
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+// LDS: two K-row buffers per wave, then the pair exchange. Before the loop
+// the first region holds the staged bf16 Q; after it, the merge slabs.
+constexpr int kXchOff = kWaves * 2 * kKtBytes;
+constexpr int kXchBytes = kPairs * 2 * 2 * 64 * 16;
+constexpr int kSmemBytes = kXchOff + kXchBytes;
+static_assert(2 * 2 * kHeads * kSlabRow * 4 <= kXchOff, "merge slabs fit");
+static_assert(kHeads * kStageRowU4 * 16 <= kXchOff, "staged Q fits");
+
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ v8bf as_v8bf(uint4 x) { return __builtin_bit_cast(v8bf, x); }
+__device__ __forceinline__ uint32_t h2_bits(v2h x) { return __builtin_bit_cast(uint32_t, x); }
 
-__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
-  // both values are exactly representable in bf16: keep the upper halves
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
-// 8 e2m1 codes (one dword, element 2i in the low nibble of byte i) times the
-// group scale, as 8 exact bf16
-template <int kB>
-__device__ __forceinline__ uint32_t fp4_pair_bf16(uint32_t w, float sg) {
-  const v2f f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, kB);
-  return pack_bf16_exact(f.x * sg, f.y * sg);
-}
-__device__ __forceinline__ uint4 dequant8(uint32_t w, float sg) {
-  return make_uint4(fp4_pair_bf16<0>(w, sg), fp4_pair_bf16<1>(w, sg), fp4_pair_bf16<2>(w, sg),
-                    fp4_pair_bf16<3>(w, sg));
+// 8 e2m1 codes (element 2i in the low nibble of byte i) times the group scale
+// s (both halves equal): exact fp16
+__device__ __forceinline__ uint4 fp4x8_f16(uint32_t w, v2h s) {
+  return make_uint4(h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s),
+                    h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s),
+                    h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s),
+                    h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s));
 }
 
-// 8 e4m3 codes (two dwords) as 8 exact bf16
-template <bool kHi>
-__device__ __forceinline__ uint32_t e4m3_pair_bf16(uint32_t w) {
-  const v2f f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHi);
-  return pack_bf16_exact(f.x, f.y);
-}
-__device__ __forceinline__ uint4 e4m3x8_bf16(uint32_t w0, uint32_t w1) {
-  return make_uint4(e4m3_pair_bf16<false>(w0), e4m3_pair_bf16<true>(w0), e4m3_pair_bf16<false>(w1),
-                    e4m3_pair_bf16<true>(w1));
+// 8 e4m3 codes as exact fp16
+__device__ __forceinline__ uint4 e4m3x8_f16(uint2 w) {
+  return make_uint4(h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, false)),
+                    h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, true)),
+                    h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, false)),
+                    h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true)));
 }
 
-__device__ __forceinline__ float e4m3_byte(uint32_t w, int byte) {
-  const v2f f = __builtin_amdgcn_cvt_pk_f32_fp8((int)((w >> (8 * byte)) & 0xFFu), false);
-  return f.x;
+// 8 bf16 (one uint4) times 2^k, rounded to fp16
+__device__ __forceinline__ uint4 bf16x8_to_f16(uint4 x, int k) {
+  uint32_t r[4];
+  const uint32_t in[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v2h h = {(_Float16)__builtin_ldexpf(bf16lo(in[i]), k), (_Float16)__builtin_ldexpf(bf16hi(in[i]), k)};
+    r[i] = h2_bits(h);
+  }
+  return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
-__global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(2)))
-void mla_decode_kernel(DecodeMlaLaunch a, int splits, int pages_per_split) {
-  __shared__ __align__(16) uint8_t smem[kMW * kHeads * kRowB];
-  __shared__ __align__(16) uint8_t qs[kHeads * kQRowB];   // Q, bf16 [head][576]
-  __shared__ float s_m[kMW][kHeads], s_l[kMW][kHeads];
+__device__ __forceinline__ uint32_t bf16x2_absmax(uint32_t w) {
+  return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
+}
+
+__device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
+
+// One wave's share of a page's record bytes, as loaded (coalesced: lane l
+// holds 16 bytes; see fetch): latent nibbles of the wave's 256 dims, then
+// four 16-byte chunks per key: group scales, the chunk holding s2, and the
+// wave's 32 RoPE codes.
+struct PageRaw {
+  v4u nib[2];
+  v4u tail;
+};
+
+// the same bytes in the MFMA layout (lane = key `row`, dim group `grp`)
+struct PageOp {
+  v4u nib[2];      // e2m1 codes of dims 64*grp .. +64 of the wave's 256
+  uint32_t sc;     // their four group scales
+  uint2 rp;        // RoPE codes of dims 32*half + 8*grp .. +8
+  float s2;        // the key's outer scale
+};
+
+// LDS staging of one wave's page bytes inside its current K-row buffer
+// (read back before the dequant overwrites it): nibbles of key r at 144*r
+// (128 bytes + pad), chunks of key r at kStageTail + 80*r (64 bytes + pad)
+constexpr int kStageNib = 144;
+constexpr int kStageTail = 16 * kStageNib;
+constexpr int kStageTailRow = 80;
+
+__global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a, int splits, int pages_per_split) {
+  __shared__ __align__(16) uint8_t smem[kSmemBytes];
+  __shared__ float s_m[kPairs][kHeads], s_l[kPairs][kHeads], s_e[kPairs][kHeads];
+  __shared__ int s_k[kHeads];
+  __shared__ int s_bt[kMaxSplitPages];                 // this split's block-table slice
+  __shared__ __align__(16) float s_s2[kWaves][2][16];  // current page: s2, s2 * 2^-Gs per key
+
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pair = wave >> 1;
+  const int half = wave & 1;
   const int row = lane & 15;      // key of the A operand / head of the output
   const int grp = lane >> 4;
   const int b = blockIdx.x / splits;
@@ -95,184 +154,351 @@ void mla_decode_kernel(DecodeMlaLaunch a, int splits, int pages_per_split) {
   const int npages = (L + 15) >> 4;
   const int p_begin = split * pages_per_split;
   const int p_end = min(npages, p_begin + pages_per_split);
-
-  // ---- Q (16 heads x 576 bf16) into LDS; the Q^T operand of head `row` for
-  // latent step c covers dims 128*grp + 8c, RoPE step r dims 512 + 16*grp + 8r
   {
-    const uint4 *qsrc = (const uint4 *)(a.q + (size_t)b * a.hq * (kLat + 64));
-    for (int c = threadIdx.x; c < kHeads * (kLat + 64) / 8; c += 64 * kMW) {
-      const int h = c / ((kLat + 64) / 8);
-      const int part = c - h * ((kLat + 64) / 8);
-      *(uint4 *)(qs + h * kQRowB + 16 * part) = qsrc[c];
-    }
+    const int32_t *bt = a.block_table + (size_t)b * a.bt_stride;
+    for (int i = threadIdx.x; i < p_end - p_begin; i += kThreads) s_bt[i] = bt[p_begin + i];
   }
-  __syncthreads();
-  const uint8_t *qrow = qs + row * kQRowB;
 
+  // ---- Q: stage bf16 in LDS, find each head's power-of-two scale k (largest
+  // element of head h times 2^k in [2^13, 2^14)), keep this lane's operands
+  // (head `row`; latent step c: dims 256*half + 64*grp + 8c; RoPE: dims
+  // 512 + 32*half + 8*grp) as fp16 Q * 2^k in registers
+  uint4 qop[8], qrope;
+  {
+    uint4 *qs = (uint4 *)smem;
+    const uint4 *qsrc = (const uint4 *)(a.q + (size_t)b * a.hq * (kLat + 64));
+    for (int c = threadIdx.x; c < kHeads * (kLat + 64) / 8; c += kThreads) {
+      const int h = c / ((kLat + 64) / 8);
+      qs[h * kStageRowU4 + (c - h * ((kLat + 64) / 8))] = qsrc[c];
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const uint4 *qr = qs + row * kStageRowU4;
+      uint32_t am = 0;
+#pragma unroll
+      for (int i = 0; i < 18; ++i) {
+        const uint4 v = qr[18 * grp + i];
+        am = max(am, max(max(bf16x2_absmax(v.x), bf16x2_absmax(v.y)), max(bf16x2_absmax(v.z), bf16x2_absmax(v.w))));
+      }
+      am = max(am, (uint32_t)__shfl_xor((int)am, 16, 64));
+      am = max(am, (uint32_t)__shfl_xor((int)am, 32, 64));
+      // amax < 2^e  ->  amax * 2^(14 - e) in [2^13, 2^14)
+      if (grp == 0) s_k[row] = am == 0 ? 0 : 14 - __builtin_amdgcn_frexp_expf(__uint_as_float(am << 16));
+    }
+    __syncthreads();
+    const uint4 *qr = qs + row * kStageRowU4;
+    const int k = s_k[row];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qop[c] = bf16x8_to_f16(qr[(kHalf * half + 64 * grp + 8 * c) / 8], k);
+    qrope = bf16x8_to_f16(qr[(kLat + 32 * half + 8 * grp) / 8], k);
+    __syncthreads();
+    // K-row buffers start at zero: the PV of a page slot that holds no page
+    // multiplies them by P = 0
+    for (int c = threadIdx.x; c < kXchOff / 16; c += kThreads) ((uint4 *)smem)[c] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+  }
+  const float c_score = __builtin_ldexpf(a.scale_log2, -s_k[row]);   // undoes 2^k of head `row`
+  const float c_rope = a.rope_scale * c_score;
+
+  // per head `row`: running integer max m (log2 units) and this lane's part
+  // of the denominator; per pair: the outer-scale exponent Gs. The
+  // accumulator holds O_acc = 2^-Gs * sum_j 2^(x_j - m) s2_j Kt_j.
   float m_run = -INFINITY;
   float l_run = 0.0f;
-  v4f o[32];
+  int Gs = kGUnset;
+  v4f o[16];
 #pragma unroll
-  for (int t = 0; t < 32; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 16; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  v4h pb_prev = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};   // P of the previous page
 
-  uint8_t *kt = smem + wave * kHeads * kRowB;
-  const int32_t *bt = a.block_table + (size_t)b * a.bt_stride;
+  // K rows, chunk-major: 16-byte chunk ch (dims 8ch .. 8ch+7 of the wave's
+  // 256) of key r sits at 256*ch + 16*(r ^ 4*(ch&1)). Row writes (8 lanes =
+  // 8 keys of one chunk) and transposed reads (16 lanes = 4 keys x 2 chunks)
+  // both cover 32 distinct banks. Buffer j of the wave is kKtBytes further.
+  uint8_t *kt = smem + wave * 2 * kKtBytes;
+  uint8_t *wbase_e = kt + 2048 * grp + 16 * row;          // even steps: chunk 8*grp + c
+  uint8_t *wbase_o = kt + 2048 * grp + 16 * (row ^ 4);    // odd steps
+  // transposed reads: lane s of group grp reads key 4*grp + s/4, dims
+  // 16q + 4(s%4) .. +4 = chunk 2q + (s%4)/2, 8-byte half (s%4)&1
+  const int rc1 = (row & 3) >> 1;
+  const uint8_t *rbase = kt + 256 * rc1 + 16 * ((4 * grp + (row >> 2)) ^ (4 * rc1)) + 8 * (row & 1);
+  v4f *xch = (v4f *)(smem + kXchOff) + pair * 2 * 2 * 64;   // [buf][half][lane]
+  // coalesced page loads: nibble load i, lane l -> key 8i + l/8, bytes
+  // 128*half + 16*(l%8); chunk load, lane l -> key l/4, chunk l%4 of
+  // {scales 256 + 16*half, s2 block 288, RoPE 304 + 32*half, +16}
+  const uint32_t off_nib = (lane >> 3) * kRec + 128 * half + 16 * (lane & 7);
+  const int tch = lane & 3;
+  const uint32_t off_tail = (lane >> 2) * kRec + (tch == 0 ? 256 + 16 * half : (tch == 1 ? 288 : 304 + 32 * half + 16 * (tch - 2)));
+  uint8_t *st_nib = kt + kStageNib * (lane >> 3) + 16 * (lane & 7);          // + 8*kStageNib for load 1
+  uint8_t *st_tail = kt + kStageTail + kStageTailRow * (lane >> 2) + 16 * tch;
+  const uint8_t *ld_nib = kt + kStageNib * row + 32 * grp;
+  const uint8_t *ld_tail = kt + kStageTail + kStageTailRow * row;
 
-  for (int p = p_begin + wave; p < p_end; p += kMW) {
-    const uint8_t *rec = a.records + (size_t)bt[p] * (16 * kRec);
-    const uint8_t *mine = rec + row * kRec;
-    const bool key_ok = p * 16 + row < L;
-    v4u nib[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) nib[i] = __builtin_nontemporal_load((const v4u *)(mine + 64 * grp + 16 * i));
-    const uint2 sc = *(const uint2 *)(mine + 256 + 8 * grp);
-    const v4u rp = __builtin_nontemporal_load((const v4u *)(mine + 304 + 16 * grp));
+  // Every page slot issues the same five loads, so the wait for one buffer
+  // never covers the later buffers' loads in flight. Without a page to fetch
+  // they read this sequence's Q block instead (18 KB, just read, unused).
+  const uint8_t *dummy = (const uint8_t *)(a.q + (size_t)b * a.hq * (kLat + 64));
+  auto fetch = [&](int p, PageRaw &r) {
+    const uint8_t *page = dummy;
+    if (p < p_end) page = a.records + (size_t)__builtin_amdgcn_readfirstlane(s_bt[p - p_begin]) * (16 * kRec);
+    r.nib[0] = __builtin_nontemporal_load((const v4u *)(page + off_nib));
+    r.nib[1] = __builtin_nontemporal_load((const v4u *)(page + off_nib + 8 * kRec));
+    r.tail = __builtin_nontemporal_load((const v4u *)(page + off_tail));
+  };
 
-    // ---- dequant + QK^T (latent), rows also to LDS for PV
-    v4f acc_lat = v4f{0.f, 0.f, 0.f, 0.f};
-    uint8_t *ktrow = kt + row * kRowB + 256 * grp;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const uint32_t w = nib[c >> 2][c & 3];
-      const float sg = e4m3_byte((c >> 1) < 4 ? sc.x : sc.y, (c >> 1) & 3);
-      uint4 x = dequant8(w, sg);
-      if (!key_ok) x = make_uint4(0, 0, 0, 0);
-      *(uint4 *)(ktrow + 16 * c) = x;
-      const uint4 qop = *(const uint4 *)(qrow + 256 * grp + 16 * c);
-      acc_lat = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(x), as_v8bf(qop), acc_lat, 0, 0, 0);
+  // Page slot k of this pair (page p = p_begin + pair + k*kPairs, if below
+  // p_end): dequant + QK^T of page k into K-row buffer k&1, interleaved with
+  // the PV of page k-1 from the other buffer; exchange of the half scores;
+  // softmax of page k. `raw` holds page k's bytes and is refilled with page
+  // k + kBufs.
+  auto step = [&](PageRaw &raw, int k) {
+    const int p = p_begin + pair + k * kPairs;
+    const bool active = p < p_end;        // uniform over the wave
+    const bool tail = (p + 1) * 16 > L;   // the sequence's last, partial page
+    const int cb = (k & 1) * kKtBytes;    // this page's K-row buffer
+    const int pbuf = kKtBytes - cb;       // the previous page's
+    // ---- page bytes to the MFMA layout through the wave's staging area
+    *(v4u *)(st_nib + cb) = raw.nib[0];
+    *(v4u *)(st_nib + cb + 8 * kStageNib) = raw.nib[1];
+    *(v4u *)(st_tail + cb) = raw.tail;
+    PageOp buf;
+    buf.nib[0] = *(const v4u *)(ld_nib + cb);
+    buf.nib[1] = *(const v4u *)(ld_nib + cb + 16);
+    buf.sc = *(const uint32_t *)(ld_tail + cb + 4 * grp);
+    buf.s2 = *(const float *)(ld_tail + cb + 16 + 4);
+    buf.rp = *(const uint2 *)(ld_tail + cb + 32 + 8 * grp);
+    // Keys past the end, and every key of a slot without a page: group
+    // scales (possibly NaN codes) and outer scale become zero, so their K
+    // rows, V rows and P entries are exactly zero; their scores are masked.
+    if (!active || (tail && p * 16 + row >= L)) {
+      buf.sc = 0u;
+      buf.s2 = 0.0f;
     }
-    // ---- RoPE part
-    v4f acc_rope = v4f{0.f, 0.f, 0.f, 0.f};
+    // ---- outer-scale exponent of the pair (both waves see the same keys);
+    // a raise rescales the accumulator after the previous page's PV
+    const int e2 = __builtin_amdgcn_frexp_expf(buf.s2);
+    int g_new = Gs;
+    if (__ballot(buf.s2 > 0.0f && e2 > Gs)) {
+      int emax = buf.s2 > 0.0f ? e2 : kGUnset;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      uint4 x = e4m3x8_bf16(rp[2 * r], rp[2 * r + 1]);
-      if (!key_ok) x = make_uint4(0, 0, 0, 0);
-      const uint4 qop = *(const uint4 *)(qrow + 2 * kLat + 32 * grp + 16 * r);
-      acc_rope = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(x), as_v8bf(qop), acc_rope, 0, 0, 0);
+      for (int msk = 1; msk < 16; msk <<= 1) emax = max(emax, __shfl_xor(emax, msk, 64));
+      g_new = __builtin_amdgcn_readfirstlane(emax);
     }
-
-    // ---- scores of keys 4*grp + i for head `row`
-    float x[4], s2v[4];
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = 4 * grp + i;
-      const bool ok = p * 16 + k < L;
-      s2v[i] = ok ? *(const float *)(rec + k * kRec + 292) : 0.0f;
-      x[i] = ok ? a.scale_log2 * fmaf(s2v[i], acc_lat[i], a.rope_scale * acc_rope[i]) : -INFINITY;
-      bmax = fmaxf(bmax, x[i]);
+    if (grp == 0) {
+      s_s2[wave][0][row] = buf.s2;
+      s_s2[wave][1][row] = __builtin_ldexpf(buf.s2, -g_new);   // < 1
     }
-    bmax = wave_max_xor(bmax, 16);
-    bmax = wave_max_xor(bmax, 32);
-    const float m_new = fmaxf(m_run, bmax);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    float pw[4], psum = 0.0f;
+    // ---- dequant + QK^T of this page, PV of the previous page
+    const v2h sg01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(buf.sc, 1.0f, false);
+    const v2h sg23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(buf.sc, 1.0f, true);
+    v4f acc_l = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pe = __builtin_amdgcn_exp2f(x[i] - m_use);
-      psum += pe;
-      pw[i] = pe * s2v[i];
-    }
-    l_run = l_run * alpha + psum;
-    typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
-    const v4bf pb4 = {(__bf16)pw[0], (__bf16)pw[1], (__bf16)pw[2], (__bf16)pw[3]};
-    const v4s pb = __builtin_bit_cast(v4s, pb4);
-    if (__ballot(alpha != 1.0f)) {
+    for (int c = 0; c < 8; ++c) {
+      const _Float16 s = (c >> 2) == 0 ? sg01[(c >> 1) & 1] : sg23[(c >> 1) & 1];
+      const uint4 x = fp4x8_f16(buf.nib[c >> 2][c & 3], v2h{s, s});
+      *(uint4 *)(((c & 1) ? wbase_o : wbase_e) + cb + 256 * c) = x;
+      acc_l = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, x), __builtin_bit_cast(v8h, qop[c]),
+                                                     acc_l, 0, 0, 0);
 #pragma unroll
-      for (int t = 0; t < 32; ++t) o[t] *= alpha;
-    }
-
-    // ---- PV: lane s of each 16-lane group fetches 8 bytes of key row
-    // 4*grp + s/4 at dims 16t + 4*(s%4); the transpose read hands lane j the
-    // dim 16t + j of keys 4*grp .. 4*grp+3
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const uint8_t *trbase = kt + (4 * grp + (row >> 2)) * kRowB + 8 * (row & 3);
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      const v4s va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s *)(trbase + 32 * t));
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[t], 0, 0, 0);
-      // bound the transpose reads in flight (each holds two registers)
-      if ((t & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
-
-  // ---- merge the waves (lane holds O[head row][dims 16t + 4*grp + i])
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (grp == 0) {
-    s_m[wave][row] = m_run;
-    s_l[wave][row] = l_run;
-  }
-  __syncthreads();
-  {
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kMW; ++w) M = fmaxf(M, s_m[w][row]);
-    const float f = __builtin_amdgcn_exp2f(m_run - (M == -INFINITY ? 0.0f : M));
-#pragma unroll
-    for (int t = 0; t < 32; ++t) o[t] *= f;
-  }
-  float *slab = (float *)smem;          // [kMW/2][16 heads][512 dims]
-  constexpr int H = kMW / 2;
-  if (wave >= H) {
-#pragma unroll
-    for (int t = 0; t < 32; ++t)
-      *(v4f *)(slab + ((size_t)(wave - H) * kHeads + row) * kLat + 16 * t + 4 * grp) = o[t];
-  }
-  __syncthreads();
-  if (wave < H) {
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      float *dst = slab + ((size_t)wave * kHeads + row) * kLat + 16 * t + 4 * grp;
-      *(v4f *)dst = o[t] + *(const v4f *)dst;
-    }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < kHeads * kLat; e += 64 * kMW) {
-    const int h = e / kLat;
-    const int d = e - h * kLat;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kMW; ++w) M = fmaxf(M, s_m[w][h]);
-    const float Mu = M == -INFINITY ? 0.0f : M;
-    float den = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kMW; ++w) den += __builtin_amdgcn_exp2f(s_m[w][h] - Mu) * s_l[w][h];
-    float acc = 0.0f;
-#pragma unroll
-    for (int w = 0; w < H; ++w) acc += slab[((size_t)w * kHeads + h) * kLat + d];
-    if (splits == 1) {
-      const float val = den > 0.0f ? acc / den : 0.0f;
-      a.out[((size_t)b * a.hq + h) * kLat + d] = (uint16_t)f32_to_bf16_bits(val);
-    } else {
-      const size_t pi = ((size_t)b * a.hq + h) * splits + split;
-      a.part_o[pi * kLat + d] = acc;
-      if (d == 0) {
-        a.part_ml[2 * pi] = M;
-        a.part_ml[2 * pi + 1] = den;
+      for (int j = 0; j < 2; ++j) {
+        const int q = 2 * c + j;   // PV tile: dims 16q .. 16q+15
+        const v4s va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s *)(rbase + pbuf + 512 * q));
+        o[q] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h, va), pb_prev, o[q], 0, 0, 0);
       }
     }
+    const uint4 xr = e4m3x8_f16(buf.rp);
+    const v4f acc_r = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xr), __builtin_bit_cast(v8h, qrope),
+                                                             v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    if (g_new != Gs) {
+      const float f = __builtin_ldexpf(1.0f, max(Gs - g_new, -200));
+#pragma unroll
+      for (int q = 0; q < 16; ++q) o[q] *= f;
+      Gs = g_new;
+    }
+    // this wave's part of the log2-domain scores of keys 4*grp + i, head `row`
+    const v4f s2v = *(const v4f *)&s_s2[wave][0][4 * grp];
+    v4f y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = fmaf(c_score * s2v[i], acc_l[i], c_rope * acc_r[i]);
+    xch[(k & 1) * 128 + half * 64 + lane] = y;
+    __syncthreads();
+    fetch(p + kBufs * kPairs, raw);
+
+    // ---- softmax of keys 4*grp + i for head `row` (identical in both waves)
+    pb_prev = v4h{(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
+    if (!active) return;
+    const v4f y0 = xch[(k & 1) * 128 + lane];
+    const v4f y1 = xch[(k & 1) * 128 + 64 + lane];
+    const v4f s2p = *(const v4f *)&s_s2[wave][1][4 * grp];
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = y0[i] + y1[i];
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (p * 16 + 4 * grp + i >= L) x[i] = -INFINITY;
+    }
+    bool raise_m = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raise_m |= x[i] > m_run + kTau;
+    if (__ballot(raise_m)) {
+      float bmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      bmax = xor_max(xor_max(bmax, 16), 32);
+      if (bmax > m_run + kTau) {
+        const float m_new = __builtin_ceilf(bmax);
+        const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);   // power of two
+        l_run *= alpha;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) o[q] *= alpha;
+        m_run = m_new;
+      }
+    }
+    float pw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pe = __builtin_amdgcn_exp2f(x[i] - m_run);   // <= 2^8
+      l_run += pe;
+      pw[i] = pe * s2p[i];
+    }
+    pb_prev = v4h{(_Float16)pw[0], (_Float16)pw[1], (_Float16)pw[2], (_Float16)pw[3]};
+  };
+
+  const int iters = p_end > p_begin ? (p_end - p_begin + kPairs - 1) / kPairs : 0;
+  PageRaw buf0, buf1, buf2, buf3;
+  fetch(p_begin + pair, buf0);
+  fetch(p_begin + pair + kPairs, buf1);
+  fetch(p_begin + pair + 2 * kPairs, buf2);
+  fetch(p_begin + pair + 3 * kPairs, buf3);
+  int it = 0;
+  for (; it + 3 < iters; it += 4) {
+    step(buf0, it);
+    step(buf1, it + 1);
+    step(buf2, it + 2);
+    step(buf3, it + 3);
   }
+  if (it < iters) step(buf0, it);
+  if (it + 1 < iters) step(buf1, it + 1);
+  if (it + 2 < iters) step(buf2, it + 2);
+  // PV of the last page slot (K-row buffer (iters - 1) & 1; P is zero if
+  // that slot held no page or there was none)
+  {
+    const int pbuf = ((iters - 1) & 1) * kKtBytes;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const v4s va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s *)(rbase + pbuf + 512 * q));
+      o[q] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h, va), pb_prev, o[q], 0, 0, 0);
+    }
+  }
+
+  // ---- merge the pairs. Pair totals per head: l_abs = 2^m l,
+  // O_abs = 2^(m + Gs) O_acc.
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  const bool has_o = m_run != -INFINITY && Gs != kGUnset;
+  const float my_e = has_o ? m_run + (float)Gs : -INFINITY;
+  if (half == 0 && grp == 0) {
+    s_m[pair][row] = m_run;
+    s_l[pair][row] = l_run;
+    s_e[pair][row] = my_e;
+  }
+  __syncthreads();   // also: every wave is past its last K-row read
+  float E = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < kPairs; ++q) E = fmaxf(E, s_e[q][row]);
+  {
+    const float f = my_e == -INFINITY ? 0.0f : __builtin_ldexpf(1.0f, max((int)(my_e - E), -200));
+#pragma unroll
+    for (int q = 0; q < 16; ++q) o[q] *= f;
+  }
+  // pairs 2, 3 hand their halves to pairs 0, 1, which add them in place; the
+  // last add happens on the way out
+  float *slab = (float *)smem;   // [2 pair slots][2 halves][16 heads][kSlabRow]
+  auto slab_at = [&](int slot, int h, int hd, int d) -> float * {
+    return slab + ((size_t)(slot * 2 + h) * kHeads + hd) * kSlabRow + d;
+  };
+  if (pair >= 2) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) *(v4f *)slab_at(pair - 2, half, row, 16 * q + 4 * grp) = o[q];
+  }
+  __syncthreads();
+  if (pair < 2) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      v4f *dst = (v4f *)slab_at(pair, half, row, 16 * q + 4 * grp);
+      *dst = o[q] + *dst;
+    }
+  }
+  __syncthreads();
+  // output: 4 consecutive dims per thread and pass
+  for (int e4 = threadIdx.x; e4 < kHeads * kLat / 4; e4 += kThreads) {
+    const int hd = e4 / (kLat / 4);
+    const int d = 4 * (e4 - hd * (kLat / 4));
+    const int h = d / kHalf;
+    const int dd = d - h * kHalf;
+    const v4f acc = *(const v4f *)slab_at(0, h, hd, dd) + *(const v4f *)slab_at(1, h, hd, dd);
+    float Mh = -INFINITY, Eh = -INFINITY, den = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kPairs; ++q) {
+      Mh = fmaxf(Mh, s_m[q][hd]);
+      Eh = fmaxf(Eh, s_e[q][hd]);
+    }
+    if (Mh != -INFINITY) {
+#pragma unroll
+      for (int q = 0; q < kPairs; ++q)
+        if (s_m[q][hd] != -INFINITY) den += __builtin_amdgcn_exp2f(s_m[q][hd] - Mh) * s_l[q][hd];
+    }
+    if (splits == 1) {
+      float sc = 0.0f;
+      if (den > 0.0f && Eh != -INFINITY) sc = __builtin_ldexpf(1.0f / den, (int)(Eh - Mh));
+      uint2 w;
+      w.x = f32_to_bf16_bits(acc[0] * sc) | (f32_to_bf16_bits(acc[1] * sc) << 16);
+      w.y = f32_to_bf16_bits(acc[2] * sc) | (f32_to_bf16_bits(acc[3] * sc) << 16);
+      *(uint2 *)(a.out + ((size_t)b * a.hq + hd) * kLat + d) = w;
+    } else {
+      const size_t pi = ((size_t)b * a.hq + hd) * splits + split;
+      *(v4f *)(a.part_o + pi * kLat + d) = acc;
+      if (d == 0) *(v4f *)(a.part_ml + 4 * pi) = v4f{Mh, den, Eh, 0.0f};
+    }
+  }
+}
+
+// Split combine: per (sequence, head), out = 2^(E - M) * sum_s 2^(E_s - E) O_s
+// / sum_s 2^(M_s - M) den_s. Splits that saw no key (M_s = -inf, den_s = 0)
+// and splits with no nonzero term (E_s = -inf) drop out.
+__global__ __launch_bounds__(kLat) void mla_combine_kernel(const float *part_o, const float *part_ml,
+                                                           uint16_t *out, int splits) {
+  const int bh = blockIdx.x;
+  const int d = threadIdx.x;
+  const float *ml = part_ml + (size_t)bh * splits * 4;
+  float M = -INFINITY, E = -INFINITY;
+  for (int s = 0; s < splits; ++s) {
+    M = fmaxf(M, ml[4 * s]);
+    E = fmaxf(E, ml[4 * s + 2]);
+  }
+  float acc = 0.0f, den = 0.0f;
+  const float *po = part_o + (size_t)bh * splits * kLat + d;
+  for (int s = 0; s < splits; ++s) {
+    if (ml[4 * s] != -INFINITY) den += __builtin_amdgcn_exp2f(ml[4 * s] - M) * ml[4 * s + 1];
+    if (ml[4 * s + 2] != -INFINITY)
+      acc += __builtin_ldexpf(po[(size_t)s * kLat], max((int)(ml[4 * s + 2] - E), -200));
+  }
+  float val = 0.0f;
+  if (den > 0.0f && E != -INFINITY) val = __builtin_ldexpf(acc / den, (int)(E - M));
+  out[(size_t)bh * kLat + d] = (uint16_t)f32_to_bf16_bits(val);
 }
 
 }  // namespace
 
 hipError_t launch_decode_mla(const DecodeMlaLaunch &a, const MlaPlan &p, hipStream_t s) {
   if (a.hq != kHeads) return hipErrorNotSupported;
-  hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)((size_t)a.batch * p.splits)), dim3(64 * kMW), 0, s, a,
+  hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)((size_t)a.batch * p.splits)), dim3(kThreads), 0, s, a,
                      p.splits, p.pages_per_split);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL((split_combine_kernel<kLat>), dim3((unsigned)((size_t)a.batch * a.hq)), dim3(kLat), 0, s,
-                     a.part_o, a.part_ml, a.out, p.splits, 1.0f);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((size_t)a.batch * a.hq)), dim3(kLat), 0, s, a.part_o,
+                     a.part_ml, a.out, p.splits);
   return hipGetLastError();
 }
 

@@ -101,8 +101,10 @@ typedef struct {
   int32_t window;        /* 0: full attention; W > 0: a query at position p
                             attends keys j with p - W < j <= p (a 512-token
                             window is [PR54705] "Purpose") */
-  int32_t num_splits;    /* 0: library's choice; > 0 forces the number of
-                            KV splits per (sequence, KV head) in decode */
+  int32_t num_splits;    /* 0: library's choice; > 0 requests the number of
+                            KV splits per (sequence, KV head) in decode. The
+                            library clamps it: at least 4 pages per split,
+                            and for NVFP4 at most 512 pages per split */
   int32_t reserved;      /* must be 0 */
   float softmax_scale;   /* finite, > 0 */
   float q_scale;         /* E4M3: Q quantization scale; NVFP4: ignored */
