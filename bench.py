@@ -120,7 +120,7 @@ def copy_probe(torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build runs on a single MI355X "
+        print("bench.py measures one GPU only: the path runs on a single MI355X "
               "(no collectives or sharding); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
