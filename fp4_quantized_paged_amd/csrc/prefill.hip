@@ -15,12 +15,16 @@
 //    16-token column blocks, so one staged K/V block feeds 16 QK^T MFMAs and
 //    32 PV MFMAs per wave;
 //  * K/V advance in 128-key blocks (8 pages). The workgroup copies a block's K
-//    rows and token-minor V^T pages into LDS once (K rows bank-swizzled) while
-//    the next block's bytes are already in flight in registers;
-//  * QK^T and PV use v_mfma_f32_16x16x128_f8f6f4 with the same lane mapping as
+//    rows (bank-swizzled) and its token-minor V^T pages, converted once to
+//    bf16, into LDS while the next block's bytes are already in flight in
+//    registers;
+//  * QK^T uses v_mfma_f32_16x16x128_f8f6f4 with the same lane mapping as
 //    decode: the key rows are permuted so that the S^T output lane of query row
-//    (l % 16) holds exactly the 32 keys PV consumes from it, P = 2^8 p split
-//    into two e4m3 terms;
+//    (l % 16) holds exactly the 32 keys PV consumes from it;
+//  * PV runs on v_mfma_f32_16x16x32_bf16 with P in bf16 (exact e4m3 V, 8-bit
+//    P mantissa, fp32 accumulation); a ones tile in the same MFMA stream
+//    accumulates the row sums of the rounded P, so the normaliser matches
+//    what PV summed;
 //  * the bf16 bias of a block takes at most 159 distinct distances per head;
 //    each wave fills a small LDS table of them and looks the scores' bias up;
 //  * workgroups are numbered so that all tiles of one (sequence, KV head) land
