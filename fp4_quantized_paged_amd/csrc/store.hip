@@ -8,8 +8,9 @@
 //
 // One workgroup handles 16 consecutive input tokens. When those 16 tokens fill
 // one page in order (the bulk-prefill case), the token-minor V page image is
-// assembled in LDS and written with 16-byte stores; otherwise (decode append,
-// ragged or scattered slots) each token is written in place.
+// assembled in LDS and leaves in contiguous 16-byte stores (every store
+// instruction writes whole lines); otherwise (decode append, ragged or
+// scattered slots) each token is written in place.
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -46,7 +47,7 @@ __device__ __forceinline__ void load_chunk(const StoreE4M3Launch &a, int64_t t, 
 }
 
 __global__ __launch_bounds__(kStoreThreads) void store_e4m3_kernel(StoreE4M3Launch a, int use_lds) {
-  extern __shared__ __align__(16) uint8_t vimg[];   // [16][hkv*d] V bytes when use_lds
+  extern __shared__ __align__(16) uint8_t vimg[];   // when use_lds: [16][hkv*d] V bytes, then [hkv*d][16]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int64_t t0 = (int64_t)blockIdx.x * kPage;
@@ -104,8 +105,8 @@ __global__ __launch_bounds__(kStoreThreads) void store_e4m3_kernel(StoreE4M3Laun
     __syncthreads();
     // Stage 2: each thread takes 4 adjacent columns (head*D + dim) of the 16
     // tokens, transposes the 16x4 bytes in registers and writes four 16-byte
-    // token-minor rows. The V page image is [head][dim][16], i.e. column-major.
-    uint8_t *vpage = a.vc + (size_t)page * (size_t)row * kPage;
+    // token-minor rows to the second LDS image ([head][dim][16], the V page).
+    uint8_t *vmin = vimg + (size_t)kPage * row;
     for (int q4 = tid; q4 < (row >> 2); q4 += kStoreThreads) {
       uint32_t w[16];
 #pragma unroll
@@ -124,10 +125,14 @@ __global__ __launch_bounds__(kStoreThreads) void store_e4m3_kernel(StoreE4M3Laun
         o[3][blk] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
       }
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        __builtin_nontemporal_store(v4u{o[b][0], o[b][1], o[b][2], o[b][3]},
-                                    (v4u *)(vpage + (size_t)(4 * q4 + b) * kPage));
+      for (int b = 0; b < 4; ++b) *(v4u *)(vmin + (size_t)(4 * q4 + b) * kPage) = v4u{o[b][0], o[b][1], o[b][2], o[b][3]};
     }
+    __syncthreads();
+    // Stage 3: the page image leaves with consecutive lanes on consecutive
+    // 16-byte rows.
+    uint8_t *vpage = a.vc + (size_t)page * (size_t)row * kPage;
+    for (int c = tid; c < row; c += kStoreThreads)
+      __builtin_nontemporal_store(*(const v4u *)(vmin + (size_t)c * kPage), (v4u *)(vpage + (size_t)c * kPage));
     return;
   }
 
@@ -168,10 +173,10 @@ __global__ __launch_bounds__(kStoreThreads) void store_e4m3_kernel(StoreE4M3Laun
 
 hipError_t launch_store_e4m3(const StoreE4M3Launch &a, hipStream_t s) {
   const int64_t blocks = (a.num_tokens + kPage - 1) / kPage;
-  const size_t img = (size_t)a.hkv * a.d * kPage;
-  const int use_lds = img <= 64 * 1024;
+  const size_t img = (size_t)a.hkv * a.d * kPage;   // one V page image
+  const int use_lds = 2 * img <= 64 * 1024;
   hipLaunchKernelGGL(store_e4m3_kernel, dim3((unsigned)blocks), dim3(kStoreThreads),
-                     use_lds ? img : 0, s, a, use_lds);
+                     use_lds ? 2 * img : 0, s, a, use_lds);
   return hipGetLastError();
 }
 
