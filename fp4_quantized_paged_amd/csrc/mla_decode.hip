@@ -125,6 +125,7 @@ struct PageOp {
   uint32_t sc;     // their four group scales
   uint2 rp;        // RoPE codes of dims 32*half + 8*grp .. +8
   float s2;        // the key's outer scale
+  float s2k[4];    // outer scales of keys 4*grp + i (this lane's scores)
 };
 
 // LDS staging of one wave's page bytes inside its current K-row buffer
@@ -139,7 +140,6 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   __shared__ float s_m[kPairs][kHeads], s_l[kPairs][kHeads], s_e[kPairs][kHeads];
   __shared__ int s_k[kHeads];
   __shared__ int s_bt[kMaxSplitPages];                 // this split's block-table slice
-  __shared__ __align__(16) float s_s2[kWaves][2][16];  // current page: s2, s2 * 2^-Gs per key
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -246,56 +246,63 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     r.tail = __builtin_nontemporal_load((const v4u *)(page + off_tail));
   };
 
+  // A page's bytes to the MFMA layout through the wave's staging area in
+  // K-row buffer kb (whose rows are no longer read).
+  auto stage = [&](const PageRaw &raw, int kb, PageOp &op) {
+    *(v4u *)(st_nib + kb) = raw.nib[0];
+    *(v4u *)(st_nib + kb + 8 * kStageNib) = raw.nib[1];
+    *(v4u *)(st_tail + kb) = raw.tail;
+    op.nib[0] = *(const v4u *)(ld_nib + kb);
+    op.nib[1] = *(const v4u *)(ld_nib + kb + 16);
+    op.sc = *(const uint32_t *)(ld_tail + kb + 4 * grp);
+    op.s2 = *(const float *)(ld_tail + kb + 16 + 4);
+    op.rp = *(const uint2 *)(ld_tail + kb + 32 + 8 * grp);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) op.s2k[i] = *(const float *)(kt + kb + kStageTail + kStageTailRow * (4 * grp + i) + 20);
+  };
+
   // Page slot k of this pair (page p = p_begin + pair + k*kPairs, if below
-  // p_end): dequant + QK^T of page k into K-row buffer k&1, interleaved with
-  // the PV of page k-1 from the other buffer; exchange of the half scores;
-  // softmax of page k. `raw` holds page k's bytes and is refilled with page
-  // k + kBufs.
-  auto step = [&](PageRaw &raw, int k) {
+  // p_end): dequant + QK^T of page k (bytes in `op`) into K-row buffer k&1,
+  // interleaved with the PV of page k-1 from the other buffer; exchange of
+  // the half scores; then, while the softmax of page k runs, the bytes of
+  // slot k+1 (`raw`) are staged into the other buffer into `op`, and `raw`
+  // is refilled with slot k+1+kBufs.
+  auto step = [&](PageOp &op, int k, PageRaw &raw) {
     const int p = p_begin + pair + k * kPairs;
     const bool active = p < p_end;        // uniform over the wave
     const bool tail = (p + 1) * 16 > L;   // the sequence's last, partial page
     const int cb = (k & 1) * kKtBytes;    // this page's K-row buffer
-    const int pbuf = kKtBytes - cb;       // the previous page's
-    // ---- page bytes to the MFMA layout through the wave's staging area
-    *(v4u *)(st_nib + cb) = raw.nib[0];
-    *(v4u *)(st_nib + cb + 8 * kStageNib) = raw.nib[1];
-    *(v4u *)(st_tail + cb) = raw.tail;
-    PageOp buf;
-    buf.nib[0] = *(const v4u *)(ld_nib + cb);
-    buf.nib[1] = *(const v4u *)(ld_nib + cb + 16);
-    buf.sc = *(const uint32_t *)(ld_tail + cb + 4 * grp);
-    buf.s2 = *(const float *)(ld_tail + cb + 16 + 4);
-    buf.rp = *(const uint2 *)(ld_tail + cb + 32 + 8 * grp);
+    const int pbuf = kKtBytes - cb;       // the previous page's, and the next's
     // Keys past the end, and every key of a slot without a page: group
-    // scales (possibly NaN codes) and outer scale become zero, so their K
+    // scales (possibly NaN codes) and outer scales become zero, so their K
     // rows, V rows and P entries are exactly zero; their scores are masked.
-    if (!active || (tail && p * 16 + row >= L)) {
-      buf.sc = 0u;
-      buf.s2 = 0.0f;
+    if (!active || tail) {
+      if (!active || p * 16 + row >= L) {
+        op.sc = 0u;
+        op.s2 = 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!active || p * 16 + 4 * grp + i >= L) op.s2k[i] = 0.0f;
     }
     // ---- outer-scale exponent of the pair (both waves see the same keys);
     // a raise rescales the accumulator after the previous page's PV
-    const int e2 = __builtin_amdgcn_frexp_expf(buf.s2);
+    const int e2 = __builtin_amdgcn_frexp_expf(op.s2);
     int g_new = Gs;
-    if (__ballot(buf.s2 > 0.0f && e2 > Gs)) {
-      int emax = buf.s2 > 0.0f ? e2 : kGUnset;
+    if (__ballot(op.s2 > 0.0f && e2 > Gs)) {
+      int emax = op.s2 > 0.0f ? e2 : kGUnset;
 #pragma unroll
       for (int msk = 1; msk < 16; msk <<= 1) emax = max(emax, __shfl_xor(emax, msk, 64));
       g_new = __builtin_amdgcn_readfirstlane(emax);
     }
-    if (grp == 0) {
-      s_s2[wave][0][row] = buf.s2;
-      s_s2[wave][1][row] = __builtin_ldexpf(buf.s2, -g_new);   // < 1
-    }
     // ---- dequant + QK^T of this page, PV of the previous page
-    const v2h sg01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(buf.sc, 1.0f, false);
-    const v2h sg23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(buf.sc, 1.0f, true);
+    const v2h sg01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(op.sc, 1.0f, false);
+    const v2h sg23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(op.sc, 1.0f, true);
     v4f acc_l = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const _Float16 s = (c >> 2) == 0 ? sg01[(c >> 1) & 1] : sg23[(c >> 1) & 1];
-      const uint4 x = fp4x8_f16(buf.nib[c >> 2][c & 3], v2h{s, s});
+      const uint4 x = fp4x8_f16(op.nib[c >> 2][c & 3], v2h{s, s});
       *(uint4 *)(((c & 1) ? wbase_o : wbase_e) + cb + 256 * c) = x;
       acc_l = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, x), __builtin_bit_cast(v8h, qop[c]),
                                                      acc_l, 0, 0, 0);
@@ -307,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
         o[q] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h, va), pb_prev, o[q], 0, 0, 0);
       }
     }
-    const uint4 xr = e4m3x8_f16(buf.rp);
+    const uint4 xr = e4m3x8_f16(op.rp);
     const v4f acc_r = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xr), __builtin_bit_cast(v8h, qrope),
                                                              v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     if (g_new != Gs) {
@@ -317,20 +324,25 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
       Gs = g_new;
     }
     // this wave's part of the log2-domain scores of keys 4*grp + i, head `row`
-    const v4f s2v = *(const v4f *)&s_s2[wave][0][4 * grp];
     v4f y;
+    float s2p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = fmaf(c_score * s2v[i], acc_l[i], c_rope * acc_r[i]);
+    for (int i = 0; i < 4; ++i) {
+      y[i] = fmaf(c_score * op.s2k[i], acc_l[i], c_rope * acc_r[i]);
+      s2p[i] = __builtin_ldexpf(op.s2k[i], -Gs);   // < 1
+    }
     xch[(k & 1) * 128 + half * 64 + lane] = y;
     __syncthreads();
-    fetch(p + kBufs * kPairs, raw);
+    // ---- next slot's bytes: staged into buffer (k+1)&1 (the PV above was
+    // its last reader); its load buffer is refilled right away
+    stage(raw, pbuf, op);
+    fetch(p + (kBufs + 1) * kPairs, raw);
 
     // ---- softmax of keys 4*grp + i for head `row` (identical in both waves)
     pb_prev = v4h{(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
     if (!active) return;
     const v4f y0 = xch[(k & 1) * 128 + lane];
     const v4f y1 = xch[(k & 1) * 128 + 64 + lane];
-    const v4f s2p = *(const v4f *)&s_s2[wave][1][4 * grp];
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = y0[i] + y1[i];
@@ -370,16 +382,19 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   fetch(p_begin + pair + kPairs, buf1);
   fetch(p_begin + pair + 2 * kPairs, buf2);
   fetch(p_begin + pair + 3 * kPairs, buf3);
+  PageOp op;
+  stage(buf0, 0, op);   // slot 0 into K-row buffer 0
+  fetch(p_begin + pair + kBufs * kPairs, buf0);
   int it = 0;
   for (; it + 3 < iters; it += 4) {
-    step(buf0, it);
-    step(buf1, it + 1);
-    step(buf2, it + 2);
-    step(buf3, it + 3);
+    step(op, it, buf1);
+    step(op, it + 1, buf2);
+    step(op, it + 2, buf3);
+    step(op, it + 3, buf0);
   }
-  if (it < iters) step(buf0, it);
-  if (it + 1 < iters) step(buf1, it + 1);
-  if (it + 2 < iters) step(buf2, it + 2);
+  if (it < iters) step(op, it, buf1);
+  if (it + 1 < iters) step(op, it + 1, buf2);
+  if (it + 2 < iters) step(op, it + 2, buf3);
   // PV of the last page slot (K-row buffer (iters - 1) & 1; P is zero if
   // that slot held no page or there was none)
   {
