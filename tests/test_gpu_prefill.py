@@ -35,6 +35,7 @@ CASES = [
     ([777], [129], 8, 1, 0, True),                   # one KV head, group 8
     ([260, 90], [70, 90], 12, 3, 0, True),           # group 4: half the waves idle
     ([200], [45], 32, 2, 0, True),                   # group 16: two head blocks
+    ([100, 50, 33], [0, 50, 0], 8, 2, 0, True),      # sequences without new tokens
 ]
 
 

@@ -58,6 +58,26 @@ def test_store_all_bf16_patterns(scales, layout):
     assert ok_v.all(), np.argwhere(~ok_v)[:5]
 
 
+@pytest.mark.parametrize("hkv", [16, 32])
+def test_store_wide_rows(hkv):
+    """Whole pages in order with 16 and 32 KV heads of 128 dims: the largest
+    row whose two V page images fit the staged path, and one that takes the
+    in-place path."""
+    d, T = 128, 96
+    rng = np.random.default_rng(hkv)
+    k = bf16(rng.standard_normal((T, hkv, d)).astype(np.float32) * 3.0)
+    v = bf16(rng.standard_normal((T, hkv, d)).astype(np.float32) * 8.0)
+    num_pages = T // 16 + 3
+    slot = np.arange(T, dtype=np.int64) + 32
+    cache = kvq.E4M3Cache(num_pages, hkv, d)
+    kvq.store(cache, k.cuda(), v.cuda(), torch.from_numpy(slot).cuda(), 0.05, 0.1)
+    torch.cuda.synchronize()
+    kc, vc = new_cache(num_pages, hkv, 16, d)
+    store_e4m3(kc, vc, k.float().numpy(), v.float().numpy(), slot, 0.05, 0.1)
+    assert np.array_equal(cache.k.cpu().numpy(), kc)
+    assert np.array_equal(cache.v.cpu().numpy(), vc)
+
+
 def test_store_tiny_decode_config_bytes():
     c = config_tiny_decode()
     dc = DeviceCase(c)
