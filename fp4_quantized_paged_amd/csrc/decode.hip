@@ -56,17 +56,29 @@ __device__ __forceinline__ void page_byte_mask(int page_pos0, int lo, int hi, ui
   }
 }
 
+// LDS of one workgroup: with head_dim 128, a 16 KB K staging area per wave
+// during the key loop; after it, the wave merge ([max(W/2,1)][16][D] o) in
+// the same bytes; then [W][16] m and l.
+template <int D, int W>
+struct DecodeSmem {
+  static constexpr int kStageBytes = D == 128 ? 16384 : 0;
+  static constexpr int kMergeBytes = (W > 1 ? W / 2 : 1) * 16 * D * 4;
+  static constexpr int kRegion = W * kStageBytes > kMergeBytes ? W * kStageBytes : kMergeBytes;
+  static constexpr int kBytes = kRegion + 2 * W * 16 * 4;
+};
+
 template <int D, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_e4m3_kernel(DecodeE4M3Launch a, int splits,
                                                             int blocks_per_split, int qtiles) {
   constexpr int kTiles = DecodeTile<D>::kTiles;
-  extern __shared__ __align__(16) float smem[];   // [max(W/2,1)][16][D] o, [W][16] m, [W][16] l
-  float *s_o = smem;
-  float *s_m = smem + (W > 1 ? W / 2 : 1) * 16 * D;
+  using Sm = DecodeSmem<D, W>;
+  __shared__ __align__(16) uint8_t smem[Sm::kBytes];
+  float *s_o = (float *)smem;
+  float *s_m = (float *)(smem + Sm::kRegion);
   float *s_l = s_m + W * 16;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane & 15;      // query row (B/N index) and A-row index
   const int grp = lane >> 4;      // K-slice / key-group index
 
@@ -133,18 +145,46 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const bool edge = (pbase * 16 < lo) || ((pbase + 8) * 16 > L);
 
     // ---- K operands: MFMA j takes token 4*(j%4) + (row%4) of page (j<4 ? kp0 : kp1)
-    const uint8_t *kb0 = a.kc + (size_t)kphys0 * page_stride + g_off + (row & 3) * D + grp * 32;
-    const uint8_t *kb1 = a.kc + (size_t)kphys1 * page_stride + g_off + (row & 3) * D + grp * 32;
     v8i kop[8];
+    if constexpr (D == 128) {
+      // Whole-line loads through LDS: load i brings rows 8*(i&1) .. +8 of
+      // block page i/2 (1 KB contiguous), 16-byte chunks XOR-swizzled by
+      // (token & 3) and bit 1 of the page so that these row writes and the
+      // operand reads below both hit 32 distinct banks per 8 lanes.
+      uint8_t *kst = smem + wave * Sm::kStageBytes;
+      v4u kl[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (D == 128 || grp < 2) {
-        const uint8_t *src = (j < 4 ? kb0 : kb1) + 4 * (j & 3) * D;
-        const v4u x0 = __builtin_nontemporal_load((const v4u *)src);
-        const v4u x1 = __builtin_nontemporal_load((const v4u *)(src + 16));
+      for (int i = 0; i < 16; ++i) {
+        const int kphys = __builtin_amdgcn_readfirstlane(bt[min(pbase + i / 2, page_hi - 1)]);
+        kl[i] = __builtin_nontemporal_load(
+            (const v4u *)(a.kc + (size_t)kphys * page_stride + g_off + (8 * (i & 1) + (lane >> 3)) * 128 + 16 * (lane & 7)));
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int slot = (lane & 7) ^ ((lane >> 3) & 3) ^ (4 * ((i >> 2) & 1));
+        *(v4u *)(kst + (i / 2) * 2048 + (8 * (i & 1) + (lane >> 3)) * 128 + 16 * slot) = kl[i];
+      }
+      const int rswz = (row & 3) | (((row >> 2) & 1) << 2);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint8_t *src = kst + (2 * (row >> 2) + (j >> 2)) * 2048 + (4 * (j & 3) + (row & 3)) * 128;
+        const v4u x0 = *(const v4u *)(src + 16 * ((2 * grp) ^ rswz));
+        const v4u x1 = *(const v4u *)(src + 16 * ((2 * grp + 1) ^ rswz));
         kop[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      } else {
-        kop[j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    } else {
+      const uint8_t *kb0 = a.kc + (size_t)kphys0 * page_stride + g_off + (row & 3) * D + grp * 32;
+      const uint8_t *kb1 = a.kc + (size_t)kphys1 * page_stride + g_off + (row & 3) * D + grp * 32;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (grp < 2) {
+          const uint8_t *src = (j < 4 ? kb0 : kb1) + 4 * (j & 3) * D;
+          const v4u x0 = __builtin_nontemporal_load((const v4u *)src);
+          const v4u x1 = __builtin_nontemporal_load((const v4u *)(src + 16));
+          kop[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        } else {
+          kop[j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        }
       }
     }
     // ---- V^T operands: tile t, dim 16t + row, 16 tokens of vp0 then of vp0+1
@@ -319,8 +359,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 template <int D, int W>
 hipError_t launch_decode_t(const DecodeE4M3Launch &a, const DecodePlan &p, hipStream_t s) {
   const size_t grid = (size_t)a.batch * a.hkv * p.qtiles * p.splits;
-  const size_t lds = sizeof(float) * ((size_t)(W > 1 ? W / 2 : 1) * 16 * D + 2 * W * 16);
-  hipLaunchKernelGGL((decode_e4m3_kernel<D, W>), dim3((unsigned)grid), dim3(64 * W), lds, s, a,
+  hipLaunchKernelGGL((decode_e4m3_kernel<D, W>), dim3((unsigned)grid), dim3(64 * W), 0, s, a,
                      p.splits, p.blocks_per_split, p.qtiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
