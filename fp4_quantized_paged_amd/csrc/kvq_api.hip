@@ -97,15 +97,19 @@ kvq::DecodePlan plan_decode(const kvq_cache *c, int32_t num_seqs, int32_t max_se
   return pl;
 }
 
+// NVFP4 decode: 64 splits of at most 512 pages
+constexpr int64_t kMlaMaxSeqLen = 64 * 512 * 16;
+
 kvq::MlaPlan plan_mla(int32_t num_seqs, int32_t max_seq_len, const kvq_attn_params *p) {
   kvq::MlaPlan pl{};
   const int64_t pages = max_seq_len > 0 ? (static_cast<int64_t>(max_seq_len) + 15) / 16 : 1;
-  const int64_t target = static_cast<int64_t>(current_cu_count());   // one 12-wave workgroup per CU
+  const int64_t target = static_cast<int64_t>(current_cu_count());   // one workgroup per CU
   int64_t splits = p->num_splits > 0 ? p->num_splits : (target + num_seqs - 1) / (num_seqs > 0 ? num_seqs : 1);
   // at least 4 pages (64 keys) per split, at most 512 (the kernel stages a
-  // split's block-table slice in LDS)
+  // split's block-table slice in LDS); at most 64 splits (the combine)
   const int64_t max_splits = (pages + 3) / 4;
   if (splits > max_splits) splits = max_splits;
+  if (splits > 64) splits = 64;
   if (splits < (pages + 511) / 512) splits = (pages + 511) / 512;
   if (splits < 1) splits = 1;
   pl.pages_per_split = static_cast<int>((pages + splits - 1) / splits);
@@ -252,6 +256,7 @@ int kvq_paged_attn_decode(const kvq_cache *cache, const void *q, const int32_t *
     return hip_status(kvq::launch_decode_e4m3(a, pl, reinterpret_cast<hipStream_t>(stream)));
   }
   if (params->num_q_heads != 16) return KVQ_ERR_UNSUPPORTED;
+  if (max_seq_len > kMlaMaxSeqLen) return KVQ_ERR_UNSUPPORTED;
   const kvq::MlaPlan pl = plan_mla(num_seqs, max_seq_len, params);
   if (pl.workspace > 0 && (workspace == nullptr || workspace_bytes < pl.workspace)) return KVQ_ERR_WORKSPACE;
   if (pl.workspace > 0 && !aligned16(workspace)) return KVQ_ERR_INVALID_ARG;

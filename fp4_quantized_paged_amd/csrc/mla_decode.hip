@@ -481,27 +481,47 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
 
 // Split combine: per (sequence, head), out = 2^(E - M) * sum_s 2^(E_s - E) O_s
 // / sum_s 2^(M_s - M) den_s. Splits that saw no key (M_s = -inf, den_s = 0)
-// and splits with no nonzero term (E_s = -inf) drop out.
-__global__ __launch_bounds__(kLat) void mla_combine_kernel(const float *part_o, const float *part_ml,
-                                                           uint16_t *out, int splits) {
+// and splits with no nonzero term (E_s = -inf) drop out. One thread per 4
+// dims; every split's partial is requested before any is used.
+constexpr int kCombineThreads = kLat / 4;
+constexpr int kMaxCombineSplits = 64;
+__global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const float *part_o, const float *part_ml,
+                                                                      uint16_t *out, int splits) {
+  __shared__ float s_w[2][kMaxCombineSplits];   // per split: O weight, denominator weight
+  __shared__ float s_f;                          // 2^(E - M) / den, or 0
   const int bh = blockIdx.x;
-  const int d = threadIdx.x;
+  const int t = threadIdx.x;
   const float *ml = part_ml + (size_t)bh * splits * 4;
-  float M = -INFINITY, E = -INFINITY;
-  for (int s = 0; s < splits; ++s) {
-    M = fmaxf(M, ml[4 * s]);
-    E = fmaxf(E, ml[4 * s + 2]);
+  if (t < 64) {
+    float M = -INFINITY, E = -INFINITY;
+    const v4f r = t < splits ? *(const v4f *)(ml + 4 * t) : v4f{-INFINITY, 0.f, -INFINITY, 0.f};
+    M = r[0];
+    E = r[2];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      M = fmaxf(M, __shfl_xor(M, m, 64));
+      E = fmaxf(E, __shfl_xor(E, m, 64));
+    }
+    float wd = 0.0f, wo = 0.0f;
+    if (t < splits) {
+      if (r[0] != -INFINITY) wd = __builtin_amdgcn_exp2f(r[0] - M) * r[1];
+      if (r[2] != -INFINITY) wo = __builtin_ldexpf(1.0f, max((int)(r[2] - E), -200));
+      s_w[0][t] = wo;
+    }
+    float den = wd;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) den += __shfl_xor(den, m, 64);
+    if (t == 0) s_f = (den > 0.0f && E != -INFINITY) ? __builtin_ldexpf(1.0f / den, (int)(E - M)) : 0.0f;
   }
-  float acc = 0.0f, den = 0.0f;
-  const float *po = part_o + (size_t)bh * splits * kLat + d;
-  for (int s = 0; s < splits; ++s) {
-    if (ml[4 * s] != -INFINITY) den += __builtin_amdgcn_exp2f(ml[4 * s] - M) * ml[4 * s + 1];
-    if (ml[4 * s + 2] != -INFINITY)
-      acc += __builtin_ldexpf(po[(size_t)s * kLat], max((int)(ml[4 * s + 2] - E), -200));
-  }
-  float val = 0.0f;
-  if (den > 0.0f && E != -INFINITY) val = __builtin_ldexpf(acc / den, (int)(E - M));
-  out[(size_t)bh * kLat + d] = (uint16_t)f32_to_bf16_bits(val);
+  __syncthreads();
+  const float *po = part_o + (size_t)bh * splits * kLat + 4 * t;
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < splits; ++s) acc += s_w[0][s] * *(const v4f *)(po + (size_t)s * kLat);
+  const float f = s_f;
+  uint2 w;
+  w.x = f32_to_bf16_bits(acc[0] * f) | (f32_to_bf16_bits(acc[1] * f) << 16);
+  w.y = f32_to_bf16_bits(acc[2] * f) | (f32_to_bf16_bits(acc[3] * f) << 16);
+  *(uint2 *)(out + (size_t)bh * kLat + 4 * t) = w;
 }
 
 }  // namespace
@@ -512,8 +532,8 @@ hipError_t launch_decode_mla(const DecodeMlaLaunch &a, const MlaPlan &p, hipStre
                      p.splits, p.pages_per_split);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((size_t)a.batch * a.hq)), dim3(kLat), 0, s, a.part_o,
-                     a.part_ml, a.out, p.splits);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((size_t)a.batch * a.hq)), dim3(kCombineThreads), 0, s,
+                     a.part_o, a.part_ml, a.out, p.splits);
   return hipGetLastError();
 }
 

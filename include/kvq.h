@@ -174,7 +174,8 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t num_seqs,
  * KVQ_FMT_NVFP4_MLA368 ([PR189]): q bf16 [num_seqs][num_q_heads][576], not
  *   quantized; K = [latent ; RoPE] decoded from the records (latent =
  *   e2m1 * group scale * record outer scale, RoPE = e4m3 * k_scale), V =
- *   latent; out bf16 [num_seqs][num_q_heads][512].
+ *   latent; out bf16 [num_seqs][num_q_heads][512]. num_q_heads must be 16 and
+ *   max_seq_len at most 524,288 (KVQ_ERR_UNSUPPORTED otherwise).
  *
  * block_table: device int32 [num_seqs][block_table_stride], pages of each
  * sequence in order. seq_lens: device int32 [num_seqs]. max_seq_len: a host

@@ -120,6 +120,14 @@ def test_decode_validation(lib):
     assert lib.kvq_decode_workspace_bytes(ctypes.byref(d), 2, 1000, ctypes.byref(params(num_splits=1))) == 0
 
 
+def test_nvfp4_decode_validation(lib):
+    nv = kvq.CacheDesc(2, 16, 1, 576, 64, FAKE, None)
+    assert decode(lib, nv, params(num_q_heads=8)) == -2                 # MLA decode takes 16 heads
+    long_len = 64 * 512 * 16 + 1                                       # past 64 splits of 512 pages
+    assert decode(lib, nv, params(num_q_heads=16), max_len=long_len, bt_stride=(long_len + 15) // 16) == -2
+    assert decode(lib, nv, params(num_q_heads=16), B=0) == 0
+
+
 def test_prefill_validation(lib):
     d = e4m3_desc()
     f = lib.kvq_paged_attn_prefill
