@@ -22,12 +22,17 @@
 //    bytes per dim per page), B = P. P = 256 * p is split into two e4m3 terms
 //    (hi = e4m3(P), lo = e4m3(P - hi)) accumulated by two MFMAs, which keeps
 //    the relative error of each weight near 2^-8 while staying on fp8 MFMA;
-//  * every lane loads its MFMA operand bytes directly from HBM with 16-byte
-//    loads (the cache layout makes each operand slice contiguous), so there
-//    is no LDS staging in the key loop; LDS is used once, to merge the waves;
-//  * W waves merge through LDS; with one split the workgroup writes bf16 out
-//    directly, otherwise (m, l, o) partials go to the workspace and the
-//    combine kernel merges them.
+//  * V^T operands come straight from HBM with 16-byte loads (the cache
+//    layout makes each operand slice contiguous). With head_dim 128 the K
+//    rows of a block are fetched as whole 128-byte lines into a per-wave LDS
+//    area and read back in the permuted operand order; head_dim 64 loads its
+//    K operand slices directly;
+//  * the page ids of a block are fetched one block ahead, one vector load for
+//    all eight pages, so that the K and V loads of a block are issued back to
+//    back with no block-table round trip in front of them;
+//  * W waves merge through LDS with a single barrier; with one split the
+//    workgroup writes bf16 out directly, otherwise (m, l, o) partials go to
+//    the workspace and the combine kernel merges them.
 #include "kvq_combine.h"
 #include "kvq_device.h"
 #include "kvq_launch.h"
@@ -56,14 +61,17 @@ __device__ __forceinline__ void page_byte_mask(int page_pos0, int lo, int hi, ui
   }
 }
 
-// LDS of one workgroup: with head_dim 128, a 16 KB K staging area per wave
-// during the key loop; after it, the wave merge ([max(W/2,1)][16][D] o) in
-// the same bytes; then [W][16] m and l.
+// LDS of one workgroup: one area per wave, its K staging (head_dim 128,
+// 16 KB) during the key loop and its unnormalised O ([16][D + 4] fp32; the
+// 16-byte row pad spreads each 8-lane group of 16-byte writes over all
+// banks) at the merge; then [W][16] m and l.
 template <int D, int W>
 struct DecodeSmem {
   static constexpr int kStageBytes = D == 128 ? 16384 : 0;
-  static constexpr int kMergeBytes = (W > 1 ? W / 2 : 1) * 16 * D * 4;
-  static constexpr int kRegion = W * kStageBytes > kMergeBytes ? W * kStageBytes : kMergeBytes;
+  static constexpr int kOStride = D + 4;
+  static constexpr int kOBytes = 16 * kOStride * 4;
+  static constexpr int kWaveBytes = kStageBytes > kOBytes ? kStageBytes : kOBytes;
+  static constexpr int kRegion = W * kWaveBytes;
   static constexpr int kBytes = kRegion + 2 * W * 16 * 4;
 };
 
@@ -73,7 +81,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   constexpr int kTiles = DecodeTile<D>::kTiles;
   using Sm = DecodeSmem<D, W>;
   __shared__ __align__(16) uint8_t smem[Sm::kBytes];
-  float *s_o = (float *)smem;
   float *s_m = (float *)(smem + Sm::kRegion);
   float *s_l = s_m + W * 16;
 
@@ -129,36 +136,58 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   const size_t g_off = (size_t)g * kv_head_stride;
   const int32_t *bt = a.block_table + (size_t)b * a.bt_stride;
 
+  // head_dim 128: lane l holds the physical page of page (l & 7) of the next
+  // block, clamped to the sequence's last page.
+  int pid_next = 0;
+  if constexpr (D == 128) {
+    if (blk_begin + wave < blk_end)
+      pid_next = bt[min(page_lo + (blk_begin + wave) * 8 + (lane & 7), page_hi - 1)];
+  }
+
   for (int blk = blk_begin + wave; blk < blk_end; blk += W) {
     const int pbase = page_lo + blk * 8;
     // Pages this lane touches: K rows come from pages pbase + 2*(row/4) + {0,1},
     // V columns (and this lane's output keys) from pages pbase + 2*grp + {0,1}.
     // Pages past the sequence end are clamped to its last page: their keys are
     // masked and their V bytes zeroed below, so every load stays unconditional.
-    const int kp0 = min(pbase + 2 * (row >> 2), page_hi - 1);
-    const int kp1 = min(pbase + 2 * (row >> 2) + 1, page_hi - 1);
     const int vp0 = pbase + 2 * grp;
-    const int kphys0 = bt[kp0];
-    const int kphys1 = bt[kp1];
-    const int vphys0 = bt[min(vp0, page_hi - 1)];
-    const int vphys1 = bt[min(vp0 + 1, page_hi - 1)];
     const bool edge = (pbase * 16 < lo) || ((pbase + 8) * 16 > L);
 
-    // ---- K operands: MFMA j takes token 4*(j%4) + (row%4) of page (j<4 ? kp0 : kp1)
+    // ---- K operands: MFMA j takes token 4*(j%4) + (row%4) of page
+    // pbase + 2*(row/4) + (j/4); V^T operands: tile t, dim 16t + row, 16
+    // tokens of vp0 then of vp0+1
     v8i kop[8];
+    v8i vop[kTiles];
     if constexpr (D == 128) {
-      // Whole-line loads through LDS: load i brings rows 8*(i&1) .. +8 of
+      // Whole-line K loads through LDS: load i brings rows 8*(i&1) .. +8 of
       // block page i/2 (1 KB contiguous), 16-byte chunks XOR-swizzled by
       // (token & 3) and bit 1 of the page so that these row writes and the
       // operand reads below both hit 32 distinct banks per 8 lanes.
-      uint8_t *kst = smem + wave * Sm::kStageBytes;
+      const int pid = pid_next;
+      int ph[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ph[i] = __builtin_amdgcn_readlane(pid, i);
+      uint8_t *kst = smem + wave * Sm::kWaveBytes;
       v4u kl[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kphys = __builtin_amdgcn_readfirstlane(bt[min(pbase + i / 2, page_hi - 1)]);
+      for (int i = 0; i < 16; ++i)
         kl[i] = __builtin_nontemporal_load(
-            (const v4u *)(a.kc + (size_t)kphys * page_stride + g_off + (8 * (i & 1) + (lane >> 3)) * 128 + 16 * (lane & 7)));
+            (const v4u *)(a.kc + (size_t)ph[i / 2] * page_stride + g_off + (8 * (i & 1) + (lane >> 3)) * 128 + 16 * (lane & 7)));
+      const int vphys0 = grp == 0 ? ph[0] : grp == 1 ? ph[2] : grp == 2 ? ph[4] : ph[6];
+      const int vphys1 = grp == 0 ? ph[1] : grp == 1 ? ph[3] : grp == 2 ? ph[5] : ph[7];
+      const uint8_t *vb0 = a.vc + (size_t)vphys0 * page_stride + g_off + row * 16;
+      const uint8_t *vb1 = a.vc + (size_t)vphys1 * page_stride + g_off + row * 16;
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) {
+        const v4u x0 = __builtin_nontemporal_load((const v4u *)(vb0 + 256 * t));
+        const v4u x1 = __builtin_nontemporal_load((const v4u *)(vb1 + 256 * t));
+        vop[t] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
       }
+      // next block's page ids (the last block re-reads its own)
+      const int nblk_next = blk + W < blk_end ? blk + W : blk;
+      pid_next = bt[min(page_lo + nblk_next * 8 + (lane & 7), page_hi - 1)];
+      // keep all of the block's loads ahead of the LDS writes that wait on them
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int slot = (lane & 7) ^ ((lane >> 3) & 3) ^ (4 * ((i >> 2) & 1));
@@ -173,6 +202,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         kop[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
       }
     } else {
+      const int kphys0 = bt[min(pbase + 2 * (row >> 2), page_hi - 1)];
+      const int kphys1 = bt[min(pbase + 2 * (row >> 2) + 1, page_hi - 1)];
+      const int vphys0 = bt[min(vp0, page_hi - 1)];
+      const int vphys1 = bt[min(vp0 + 1, page_hi - 1)];
       const uint8_t *kb0 = a.kc + (size_t)kphys0 * page_stride + g_off + (row & 3) * D + grp * 32;
       const uint8_t *kb1 = a.kc + (size_t)kphys1 * page_stride + g_off + (row & 3) * D + grp * 32;
 #pragma unroll
@@ -186,16 +219,14 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
           kop[j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
         }
       }
-    }
-    // ---- V^T operands: tile t, dim 16t + row, 16 tokens of vp0 then of vp0+1
-    const uint8_t *vb0 = a.vc + (size_t)vphys0 * page_stride + g_off + row * 16;
-    const uint8_t *vb1 = a.vc + (size_t)vphys1 * page_stride + g_off + row * 16;
-    v8i vop[kTiles];
+      const uint8_t *vb0 = a.vc + (size_t)vphys0 * page_stride + g_off + row * 16;
+      const uint8_t *vb1 = a.vc + (size_t)vphys1 * page_stride + g_off + row * 16;
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-      const v4u x0 = __builtin_nontemporal_load((const v4u *)(vb0 + 256 * t));
-      const v4u x1 = __builtin_nontemporal_load((const v4u *)(vb1 + 256 * t));
-      vop[t] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      for (int t = 0; t < kTiles; ++t) {
+        const v4u x0 = __builtin_nontemporal_load((const v4u *)(vb0 + 256 * t));
+        const v4u x1 = __builtin_nontemporal_load((const v4u *)(vb1 + 256 * t));
+        vop[t] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      }
     }
 
     // ---- S^T = K Q^T: lane holds keys (vp0 + j/4, token 4*(j%4) + i) of its query row
@@ -289,65 +320,58 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
 
-  // ---- merge the W waves through LDS (fixed order: deterministic).
-  // Lane holds O[query row][dims 16t + 4*grp + i]. Every wave first rescales
-  // to the workgroup max, then waves [H, W) hand their O to waves [0, H),
-  // which add it and publish the H partial sums.
+  // ---- merge the W waves through LDS, in wave order (deterministic). Each
+  // wave parks m, l and its unnormalised O (lane: query row, dims
+  // 16t + 4*grp + i) in its own area, which no other wave touches during the
+  // key loop, so one barrier suffices; then each thread finishes four dims of
+  // one query row.
+  {
+    float *s_ow = (float *)(smem + wave * Sm::kWaveBytes);
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) *(v4f *)(s_ow + row * Sm::kOStride + 16 * t + 4 * grp) = o[t];
+  }
   if (grp == 0) {
     s_m[wave * 16 + row] = m_run;
     s_l[wave * 16 + row] = l_run;
   }
   __syncthreads();
-  {
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w * 16 + row]);
-    const float f = __builtin_amdgcn_exp2f(m_run - (M == -INFINITY ? 0.0f : M));
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) o[t] *= f;
-  }
-  constexpr int H = W > 1 ? W / 2 : 1;
-  if (W > 1) {
-    if (wave >= H) {
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t)
-        *(v4f *)(s_o + ((size_t)(wave - H) * 16 + row) * D + 16 * t + 4 * grp) = o[t];
-    }
-    __syncthreads();
-    if (wave < H) {
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t)
-        o[t] += *(const v4f *)(s_o + ((size_t)wave * 16 + row) * D + 16 * t + 4 * grp);
-    }
-    __syncthreads();
-  }
-  if (wave < H) {
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t)
-      *(v4f *)(s_o + ((size_t)wave * 16 + row) * D + 16 * t + 4 * grp) = o[t];
-  }
-  __syncthreads();
 
+  constexpr int kQuads = D / 4;
   const int rows_here = min(16, group - qt * 16);
-  for (int e = threadIdx.x; e < rows_here * D; e += 64 * W) {
-    const int r = e / D;
-    const int dcol = e - r * D;
+  const bool out_vec = ((uintptr_t)a.out & 7) == 0;
+  for (int e = threadIdx.x; e < rows_here * kQuads; e += 64 * W) {
+    const int r = e / kQuads;
+    const int dcol = 4 * (e - r * kQuads);
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w * 16 + r]);
     const float Mu = M == -INFINITY ? 0.0f : M;
-    float acc = 0.0f, den = 0.0f;
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.0f;
 #pragma unroll
-    for (int w = 0; w < H; ++w) acc += s_o[((size_t)w * 16 + r) * D + dcol];
-#pragma unroll
-    for (int w = 0; w < W; ++w) den += __builtin_amdgcn_exp2f(s_m[w * 16 + r] - Mu) * s_l[w * 16 + r];
+    for (int w = 0; w < W; ++w) {
+      const float f = __builtin_amdgcn_exp2f(s_m[w * 16 + r] - Mu);
+      den += f * s_l[w * 16 + r];
+      acc += f * *(const v4f *)((const float *)(smem + w * Sm::kWaveBytes) + r * Sm::kOStride + dcol);
+    }
     const int h = g * group + qt * 16 + r;
     if (splits == 1) {
-      const float val = den > 0.0f ? (acc / den) * a.v_scale : 0.0f;
-      a.out[((size_t)b * a.hq + h) * D + dcol] = (uint16_t)f32_to_bf16_bits(val);
+      uint16_t *dst = a.out + ((size_t)b * a.hq + h) * D + dcol;
+      const uint32_t w0 = f32_to_bf16_bits(den > 0.0f ? (acc[0] / den) * a.v_scale : 0.0f) |
+                          (f32_to_bf16_bits(den > 0.0f ? (acc[1] / den) * a.v_scale : 0.0f) << 16);
+      const uint32_t w1 = f32_to_bf16_bits(den > 0.0f ? (acc[2] / den) * a.v_scale : 0.0f) |
+                          (f32_to_bf16_bits(den > 0.0f ? (acc[3] / den) * a.v_scale : 0.0f) << 16);
+      if (out_vec) {
+        *(uint2 *)dst = uint2{w0, w1};
+      } else {
+        dst[0] = (uint16_t)w0;
+        dst[1] = (uint16_t)(w0 >> 16);
+        dst[2] = (uint16_t)w1;
+        dst[3] = (uint16_t)(w1 >> 16);
+      }
     } else {
       const size_t pi = ((size_t)b * a.hq + h) * splits + split;
-      a.part_o[pi * D + dcol] = acc;
+      *(v4f *)(a.part_o + pi * D + dcol) = acc;
       if (dcol == 0) {
         a.part_ml[2 * pi] = M;
         a.part_ml[2 * pi + 1] = den;
