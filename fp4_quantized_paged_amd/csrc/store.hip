@@ -10,7 +10,8 @@
 // one page in order (the bulk-prefill case), the token-minor V page image is
 // assembled in LDS and leaves in contiguous 16-byte stores (every store
 // instruction writes whole lines); otherwise (decode append, ragged or
-// scattered slots) each token is written in place.
+// scattered slots) each token is written in place, its V bytes passing
+// through LDS so that each byte-store instruction covers few lines.
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -136,8 +137,56 @@ __global__ __launch_bounds__(kStoreThreads) void store_e4m3_kernel(StoreE4M3Laun
     return;
   }
 
-  // Scattered slots (decode append, ragged tails): each chunk is written in
-  // place; the slot of token i comes from lane i of this wave.
+  if (use_lds) {
+    // Scattered slots (decode append, ragged tails): K chunks go to their rows
+    // in place (16-byte stores); V bytes are staged token-major in LDS and
+    // then leave one byte per lane, consecutive lanes on consecutive dims of
+    // one token, so a store instruction covers 8 lines (a 16-byte stride)
+    // rather than 64. The slot of token i comes from lane i of each wave.
+    for (int c0 = 0; c0 < nchunk; c0 += kStoreThreads * kUnroll) {
+      if (c0 > 0) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int c = c0 + tid + u * kStoreThreads;
+          const int i = c / cpr;
+          if (c < nchunk) load_chunk(a, t0 + i, (c - i * cpr) << 4, ch[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int c = c0 + tid + u * kStoreThreads;
+        const int i = min(c / cpr, kPage - 1);
+        const int64_t sl = __shfl(my_slot, i, 64);
+        if (c >= nchunk) continue;
+        const int r = c - i * cpr;
+        const uint2 v0 = quant8_e4m3(ch[u].v0, a.v_inv), v1 = quant8_e4m3(ch[u].v1, a.v_inv);
+        *(uint4 *)(vimg + (size_t)i * row + (r << 4)) = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        if (sl < 0) continue;
+        const int h = r / cpd;
+        const int d0 = (r - h * cpd) << 4;
+        const uint2 k0 = quant8_e4m3(ch[u].k0, a.k_inv), k1 = quant8_e4m3(ch[u].k1, a.k_inv);
+        *(uint4 *)(a.kc + ((((size_t)(sl >> 4)) * a.hkv + h) * kPage + (sl & (kPage - 1))) * a.d + d0) =
+            make_uint4(k0.x, k0.y, k1.x, k1.y);
+      }
+    }
+    __syncthreads();
+    // one token per wave at a time: column col = head * d + dim of the token
+    // lands at byte 16 * col + (slot & 15) of its page
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int i = wave; i < ntok; i += kStoreThreads / 64) {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)my_slot, i);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)my_slot >> 32), i);
+      const int64_t sl = (int64_t)(((uint64_t)hi << 32) | lo);
+      if (sl < 0) continue;
+      uint8_t *dst = a.vc + (size_t)(sl >> 4) * (size_t)row * kPage + (sl & (kPage - 1));
+      const uint8_t *src = vimg + (size_t)i * row;
+#pragma unroll 8
+      for (int col = lane; col < row; col += 64) dst[(size_t)col * kPage] = src[col];
+    }
+    return;
+  }
+
+  // Rows too wide for the LDS image: each chunk is written in place.
   for (int c0 = 0; c0 < nchunk; c0 += kStoreThreads * kUnroll) {
     if (c0 > 0) {
 #pragma unroll
