@@ -266,10 +266,16 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+PRIMER_CYCLES = 4_000_000   # a GPU spin of ~2 ms: longer than the host needs to queue 20 calls
+
+
 def back_to_back_ms(torch, fn, reps):
-    """Mean time of reps back-to-back calls fn(0 .. reps-1) between one pair of
-    HIP events (for launches long enough that the host keeps ahead)."""
+    """Mean GPU time of reps back-to-back calls fn(0 .. reps-1) between one pair
+    of HIP events. A spin kernel queued first keeps the GPU busy while the host
+    queues the start event and the calls, so neither host launch time nor idle
+    GPU time falls between the events."""
     t = EventTimer(torch)
+    torch.cuda._sleep(PRIMER_CYCLES)
     s = t.start()
     for i in range(reps):
         fn(i)
@@ -277,20 +283,11 @@ def back_to_back_ms(torch, fn, reps):
     return t.mean_ms() / reps
 
 
-def timed_mean(torch, fn, reps=10, warm=2, back_to_back=False):
-    """Mean GPU time of fn(): per call between HIP events, or (back_to_back)
-    over reps consecutive calls, which keeps events from separating launches
-    of long kernels."""
+def timed_mean(torch, fn, reps=10, warm=2):
+    """Mean GPU time of fn() over reps back-to-back calls after warm calls."""
     for _ in range(warm):
         fn()
-    if back_to_back:
-        return back_to_back_ms(torch, lambda i: fn(), reps)
-    t = EventTimer(torch)
-    for _ in range(reps):
-        s = t.start()
-        fn()
-        t.stop(s)
-    return t.mean_ms()
+    return back_to_back_ms(torch, lambda i: fn(), reps)
 
 
 def extras(torch, kvq, c, k, v, q, slot, scales):
@@ -300,8 +297,7 @@ def extras(torch, kvq, c, k, v, q, slot, scales):
     T = k.shape[0]
     # bulk quant-on-store of all 524,288 tokens
     cache = kvq.E4M3Cache(c.num_pages, Hkv, D)
-    ms = timed_mean(torch, lambda: kvq.store(cache, k, v, slot, scales["k"], scales["v"]),
-                    back_to_back=True)
+    ms = timed_mean(torch, lambda: kvq.store(cache, k, v, slot, scales["k"], scales["v"]))
     sb = store_bytes(T, Hkv, D)
     rows["store_bulk"] = {"tokens": T, "us": round(ms * 1e3, 2),
                           "tokens_per_s": round(T / (ms * 1e-3), 1),
@@ -314,8 +310,7 @@ def extras(torch, kvq, c, k, v, q, slot, scales):
     rows["store_append"] = {"tokens": int(kn.shape[0]), "us": round(ms * 1e3, 2)}
     # calibration over K and V
     amax = torch.zeros(1, device=k.device)
-    ms = timed_mean(torch, lambda: (kvq.calibrate_amax(k, amax=amax), kvq.calibrate_amax(v, amax=amax)),
-                    back_to_back=True)
+    ms = timed_mean(torch, lambda: (kvq.calibrate_amax(k, amax=amax), kvq.calibrate_amax(v, amax=amax)))
     cb = 2 * k.numel() * 2
     rows["calibrate_kv"] = {"us": round(ms * 1e3, 2), "GB_s": round(cb / (ms * 1e-3) / 1e9, 1)}
     del cache
@@ -338,8 +333,7 @@ def nvfp4_rows(torch, kvq):
     kv = c.kv.to(dev)
     slot = torch.from_numpy(c.slot_mapping).to(dev)
     caches = [kvq.Nvfp4Cache(c.num_pages) for _ in range(2)]
-    ms_store = timed_mean(torch, lambda: kvq.store(caches[0], kv, None, slot, c.rope_scale), reps=5,
-                          back_to_back=True)
+    ms_store = timed_mean(torch, lambda: kvq.store(caches[0], kv, None, slot, c.rope_scale), reps=5)
     kvq.store(caches[1], kv, None, slot, c.rope_scale)
     T = int(kv.shape[0])
     del kv
@@ -353,7 +347,7 @@ def nvfp4_rows(torch, kvq):
         cache = caches[it[0] % 2]     # 2 x 193 MB alternate: more than the Infinity Cache
         it[0] += 1
         kvq.decode(cache, q, bt, sl, c.max_seq_len, c.softmax_scale, k_scale=c.rope_scale, out=out)
-    ms = timed_mean(torch, run, reps=10, back_to_back=True)
+    ms = timed_mean(torch, run, reps=10)
     L = c.max_seq_len
     by = c.batch * (L * 368 + c.num_q_heads * (576 + 512) * 2 + ((L + 15) // 16) * 4 + 4)
     sb = T * (576 * 2 + 368 + 8)
@@ -401,7 +395,7 @@ def prefill_rows(torch, kvq):
     out = torch.empty_like(q)
     ms = timed_mean(torch, lambda: kvq.prefill(cache, q, cu, c.max_q_len, bt, sl, c.max_seq_len,
                                                c.softmax_scale, sc["q"], sc["k"], sc["v"],
-                                               slopes=slopes, out=out), reps=5, back_to_back=True)
+                                               slopes=slopes, out=out), reps=5)
     fl = prefill_flops(c.seq_lens, c.q_lens, c.num_q_heads, c.head_dim)
     tf = fl / (ms * 1e-3) / 1e12
     T = int(kn.shape[0])
@@ -438,7 +432,7 @@ def long_context_rows(torch, kvq):
             cache = caches[it[0] % 2]
             it[0] += 1
             kvq.decode(cache, q, bt, sl, L, c.softmax_scale, sc["q"], sc["k"], sc["v"], window=w)
-        ms = timed_mean(torch, run, reps=10, back_to_back=True)
+        ms = timed_mean(torch, run, reps=10)
         att = min(L, w) if w else L
         by = decode_bytes(B, Hq, Hkv, D, att)
         out["long_context" + ("_window512" if w else "")] = {
