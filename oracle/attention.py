@@ -14,6 +14,12 @@ descale-handling bullets):
 Readings where the pages are silent:
   * bias(h, i, j) = bf16_RNE(fp32(slope_h) * fp32(-(p_i - j))), a per-head
     linear bias in the query-key distance, added in fp32 after the fold;
+  * the learned relative position bias (same page, "Environment": the model
+    has one; "Test Plan": relative extents 128 and 1024, and 128 with the
+    sliding window) is a bf16 table T[h][0 .. E) indexed by the query-key
+    distance: bias(h, i, j) = T[h][min(p_i - j, E - 1)], the last entry
+    serving every longer distance. It replaces the slope bias and enters at
+    the same place;
   * a query at absolute position p attends keys j <= p; with a sliding window
     W > 0 only keys with p - W < j <= p (the window includes the current
     token); W = 0 means full attention; new queries sit at the end of the
@@ -30,7 +36,9 @@ the unsplit result to rounding.
 
 Pins: tests/test_oracle_attention.py (pure-Python brute force, fold vs explicit
 dequantisation, V linearity, split invariance, window reduction, Q = 0 mean,
-single key, zero slope, repeated-KV-head GQA equivalence).
+single key, zero slope, repeated-KV-head GQA equivalence; learned table: the
+closed-form softmax of a Q = 0 case with one-hot V, and a table filled with
+the slope bias reproducing the slope path).
 """
 from __future__ import annotations
 
@@ -45,6 +53,24 @@ def relative_bias(slope: float, q_pos: np.ndarray, k_pos: np.ndarray) -> np.ndar
     dist = (np.asarray(q_pos, dtype=np.int64)[:, None] - np.asarray(k_pos, dtype=np.int64)[None, :])
     prod = np.float32(slope) * (-dist).astype(np.float32)
     return bf16_round(prod).astype(np.float64)
+
+
+def learned_bias(table_h: np.ndarray, q_pos: np.ndarray, k_pos: np.ndarray) -> np.ndarray:
+    """Learned relative bias of one head, [len(q_pos), len(k_pos)] float64:
+    entry min(p - j, E - 1) of the bf16 row table_h [E] for key j at or before
+    the query position p; keys after p (masked anyway) read entry 0."""
+    E = len(table_h)
+    dist = (np.asarray(q_pos, dtype=np.int64)[:, None] - np.asarray(k_pos, dtype=np.int64)[None, :])
+    return np.asarray(table_h, dtype=np.float64)[np.clip(dist, 0, E - 1)]
+
+
+def _bias(h: int, q_pos, k_pos, slopes, rel):
+    """The additive bias of head h, or None (at most one kind is given)."""
+    if slopes is not None:
+        return relative_bias(float(slopes[h]), q_pos, k_pos)
+    if rel is not None:
+        return learned_bias(rel[h], q_pos, k_pos)
+    return None
 
 
 def key_mask(q_pos: np.ndarray, L: int, window: int) -> np.ndarray:
@@ -72,11 +98,12 @@ def _softmax_out(s: np.ndarray, mask: np.ndarray, vals: np.ndarray):
 
 def attend_sequence(q_codes_val: np.ndarray, q_pos: np.ndarray, k_val: np.ndarray,
                     v_val: np.ndarray, fold: float, v_scale: float, window: int,
-                    slopes, q_chunk: int = 64) -> np.ndarray:
+                    slopes, q_chunk: int = 64, rel=None) -> np.ndarray:
     """Attention of one sequence's queries.
 
     q_codes_val: decoded e4m3 Q [nq, Hq, D]; k_val [L, Hkv, D] and
-    v_val [L, Hkv, Dv] decoded e4m3 (unscaled). Returns fp64 [nq, Hq, Dv]."""
+    v_val [L, Hkv, Dv] decoded e4m3 (unscaled). slopes [Hq] or rel [Hq][E]
+    (bf16 values) select the bias. Returns fp64 [nq, Hq, Dv]."""
     nq, Hq, D = q_codes_val.shape
     L, Hkv, Dv = v_val.shape
     grp = Hq // Hkv
@@ -92,15 +119,16 @@ def attend_sequence(q_codes_val: np.ndarray, q_pos: np.ndarray, k_val: np.ndarra
             g = h // grp
             raw = q_codes_val[c0:c1, h, :] @ k_val[:, g, :].T
             s = raw * fold
-            if slopes is not None:
-                s = s + relative_bias(float(slopes[h]), qp, k_pos)
+            bias = _bias(h, qp, k_pos, slopes, rel)
+            if bias is not None:
+                s = s + bias
             o, _, _ = _softmax_out(s, mask, v_val[:, g, :])
             out[c0:c1, h, :] = o * v_scale
     return out
 
 
 def attend_split(q_codes_val, q_pos, k_val, v_val, fold, v_scale, window, slopes,
-                 chunk: int) -> np.ndarray:
+                 chunk: int, rel=None) -> np.ndarray:
     """Same as attend_sequence, but over key chunks of ``chunk`` keys merged
     with the online-softmax combine."""
     nq, Hq, D = q_codes_val.shape
@@ -114,8 +142,9 @@ def attend_split(q_codes_val, q_pos, k_val, v_val, fold, v_scale, window, slopes
     for h in range(Hq):
         g = h // grp
         s = (q_codes_val[:, h, :] @ k_val[:, g, :].T) * fold
-        if slopes is not None:
-            s = s + relative_bias(float(slopes[h]), q_pos, k_pos)
+        bias = _bias(h, q_pos, k_pos, slopes, rel)
+        if bias is not None:
+            s = s + bias
         parts = []
         for j0 in range(0, L, chunk):
             j1 = min(L, j0 + chunk)
@@ -141,7 +170,7 @@ def quantize_q(q: np.ndarray, q_scale: float) -> np.ndarray:
 def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                  block_table: np.ndarray, seq_lens: np.ndarray, softmax_scale: float,
                  q_scale: float, k_scale: float, v_scale: float, window: int = 0,
-                 slopes=None, seqs=None) -> np.ndarray:
+                 slopes=None, seqs=None, rel=None) -> np.ndarray:
     """One query per sequence at position L-1. q: [B, Hq, D] float32 (bf16
     values). Returns fp64 [B, Hq, Dv] (rows of sequences not in ``seqs`` are
     left zero)."""
@@ -156,14 +185,14 @@ def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         kc, vc = gather_tokens(k_cache, v_cache, block_table[b], L)
         qv = quantize_q(q[b:b + 1], q_scale)
         out[b] = attend_sequence(qv, np.array([L - 1]), e4m3_decode(kc), e4m3_decode(vc),
-                                 fold, v_scale, window, slopes)[0]
+                                 fold, v_scale, window, slopes, rel=rel)[0]
     return out
 
 
 def paged_prefill(q: np.ndarray, cu_q_lens: np.ndarray, k_cache: np.ndarray,
                   v_cache: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray,
                   softmax_scale: float, q_scale: float, k_scale: float, v_scale: float,
-                  window: int = 0, slopes=None, rows=None) -> np.ndarray:
+                  window: int = 0, slopes=None, rows=None, rel=None) -> np.ndarray:
     """Chunked prefill: the new queries of sequence b are rows
     cu_q_lens[b]..cu_q_lens[b+1]-1 of q [sumQ, Hq, D] at positions
     L - Lq + i. ``rows`` optionally restricts the computed query rows
@@ -188,14 +217,15 @@ def paged_prefill(q: np.ndarray, cu_q_lens: np.ndarray, k_cache: np.ndarray,
         kc, vc = gather_tokens(k_cache, v_cache, block_table[b], L)
         qv = quantize_q(q[idx], q_scale)
         out[idx] = attend_sequence(qv, pos, e4m3_decode(kc), e4m3_decode(vc), fold,
-                                   v_scale, window, slopes)
+                                   v_scale, window, slopes, rel=rel)
     return out
 
 
-def brute_force(q_vals, q_pos, k_vals, v_vals, softmax_scale, window, slopes):
+def brute_force(q_vals, q_pos, k_vals, v_vals, softmax_scale, window, slopes, rel=None):
     """Pure-Python triple loop over already-dequantized values (no numpy
     reductions), for tiny inputs. q_vals [nq][Hq][D], k_vals [L][Hkv][D],
-    v_vals [L][Hkv][Dv] as nested lists of floats. Returns nested lists."""
+    v_vals [L][Hkv][Dv] as nested lists of floats; rel: per-head lists of
+    table values. Returns nested lists."""
     import math
     nq, Hq = len(q_vals), len(q_vals[0])
     L, Hkv = len(k_vals), len(k_vals[0])
@@ -216,6 +246,8 @@ def brute_force(q_vals, q_pos, k_vals, v_vals, softmax_scale, window, slopes):
                 s = acc * softmax_scale
                 if slopes is not None:
                     s += float(bf16_round(np.float32(slopes[h]) * np.float32(-(p - j))))
+                if rel is not None:
+                    s += float(rel[h][min(p - j, len(rel[h]) - 1)])
                 scores.append(s)
             if not keys:
                 row.append([0.0] * Dv)

@@ -9,7 +9,7 @@ import pytest
 from oracle.codecs import e4m3_decode, bf16_round
 from oracle.kvcache import quantize_e4m3, new_cache, store_e4m3, gather_tokens
 from oracle.attention import (attend_sequence, attend_split, brute_force, paged_decode,
-                              paged_prefill, quantize_q, relative_bias)
+                              paged_prefill, quantize_q, relative_bias, learned_bias)
 from workloads import make_attn_case, geometric_slopes
 
 
@@ -25,20 +25,29 @@ def dq(x, s):
     return e4m3_decode(quantize_e4m3(x, s))
 
 
-@pytest.mark.parametrize("window,use_slopes", [(0, False), (0, True), (5, True), (1, False)])
-def test_bruteforce_matches_vectorised(window, use_slopes):
+def rel_table(Hq, E, seed):
+    """A bf16-exact learned relative-bias table [Hq, E]."""
+    rng = np.random.default_rng(seed)
+    return bf16_round(rng.standard_normal((Hq, E)).astype(np.float32) * 2)
+
+
+@pytest.mark.parametrize("window,bias", [(0, None), (0, "slopes"), (5, "slopes"), (1, None),
+                                         (0, "rel"), (5, "rel")])
+def test_bruteforce_matches_vectorised(window, bias):
     q, k, v = tiny()
     L = k.shape[0]
     qs, ks, vs, sm = 0.5, 0.25, 1.5, 0.3
     pos = np.array([L - 3, L - 2, L - 1])
-    slopes = geometric_slopes(4) if use_slopes else None
+    slopes = geometric_slopes(4) if bias == "slopes" else None
+    rel = rel_table(4, 7, 3) if bias == "rel" else None    # extent 7 < distances up to 18
     got = attend_sequence(quantize_q(q, qs), pos, dq(k, ks), dq(v, vs), sm * qs * ks, vs,
-                          window, slopes)
+                          window, slopes, rel=rel)
     # brute force on explicitly dequantised values (scales applied per element)
     bq = (dq(q, qs) * qs).tolist()
     bk = (dq(k, ks) * ks).tolist()
     bv = (dq(v, vs) * vs).tolist()
-    want = np.array(brute_force(bq, pos, bk, bv, sm, window, slopes))
+    want = np.array(brute_force(bq, pos, bk, bv, sm, window, slopes,
+                                None if rel is None else rel.tolist()))
     assert np.max(np.abs(got - want)) < 1e-12 * max(1.0, np.max(np.abs(want)))
 
 
@@ -107,6 +116,47 @@ def test_zero_slope_equals_no_bias_and_bias_sign():
     b7 = relative_bias(0.3, np.array([7]), np.array([0]))[0, 0]
     assert b7 == float(bf16_round(np.float32(0.3) * np.float32(-7)))
     assert b7 != float(np.float32(0.3) * np.float32(-7))
+
+
+def test_learned_bias_closed_form_softmax():
+    """Q = 0: the scores are the bias alone, so with one-hot V rows the output
+    is the softmax of the table entries the keys select. Key j of a query at
+    position p reads entry min(p - j, E - 1): the current token the first
+    entry, every distance from E - 1 on the last one; heads read their own
+    rows; a window keeps only the nearest keys."""
+    L, E, Hq, D = 10, 4, 2, 16
+    T = np.array([[0.5, -1.25, 2.0, 0.75], [-3.0, 0.0, 1.5, -0.5]], np.float32)
+    rng = np.random.default_rng(11)
+    k = rng.standard_normal((L, 1, D))
+    v = np.zeros((L, 1, D))
+    v[np.arange(L), 0, np.arange(L)] = 1.0
+    q = np.zeros((1, Hq, D))
+    for window, keys in ((0, range(L)), (3, range(L - 3, L))):
+        got = attend_sequence(q, np.array([L - 1]), k, v, 0.7, 1.0, window, None, rel=T)[0]
+        for h in range(Hq):
+            e = {j: float(T[h][min(L - 1 - j, E - 1)]) for j in keys}
+            z = sum(math.exp(x) for x in e.values())
+            want = np.zeros(D)
+            for j, x in e.items():
+                want[j] = math.exp(x) / z
+            assert np.max(np.abs(got[h] - want)) < 1e-15
+    # the lookup itself: distance 0 -> entry 0, distances >= E - 1 -> entry E - 1
+    bias = learned_bias(T[0], np.array([9]), np.arange(10))
+    assert list(bias[0]) == [0.75] * 7 + [2.0, -1.25, 0.5]
+
+
+def test_learned_table_of_slope_bias_equals_slope_path():
+    """A table holding the slope bias bf16(slope * -d) for every distance
+    reproduces the slope path exactly; a shorter table (clamped distances)
+    does not."""
+    q, k, v = tiny(seed=7, L=40)
+    slopes = geometric_slopes(4)
+    args = (quantize_q(q, 1.0), np.array([37, 38, 39]), dq(k, 1.0), dq(v, 1.0), 0.3, 1.0, 0)
+    a = attend_sequence(*args, slopes)
+    for E, same in ((40, True), (64, True), (8, False)):
+        T = np.stack([relative_bias(float(sl), np.arange(E), np.zeros(1, np.int64))[:, 0] for sl in slopes])
+        b = attend_sequence(*args, None, rel=T)
+        assert np.array_equal(a, b) == same
 
 
 def test_gqa_equals_repeated_kv_heads():

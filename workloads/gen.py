@@ -109,6 +109,7 @@ class AttnCase:
     store_batches: List[np.ndarray]  # token indices per store call, in order
     window: int = 0
     slopes: Optional[np.ndarray] = None   # float32 [Hq] or None
+    rel: Optional[np.ndarray] = None      # learned relative-bias table, float32 [Hq, E] (bf16 values) or None
     softmax_scale: float = 1.0
     fixed_scales: Optional[dict] = None   # {'q','k','v'} floats, or None -> calibrate
     v_scale_override: Optional[float] = None  # fixed v_scale while k/q are calibrated
@@ -138,6 +139,17 @@ class AttnCase:
         return np.concatenate(out) if out else np.zeros(0, np.int64)
 
 
+def rel_bias_table(rng, num_heads: int, extent: int) -> np.ndarray:
+    """A learned-looking relative-bias table [num_heads, extent], bf16 values:
+    a per-head decay -a_h * log(1 + d) in the distance d (a_h geometric in
+    [0.25, 2]) plus N(0, 0.25^2) noise, so that near keys weigh more and the
+    rows are not smooth."""
+    a = np.geomspace(0.25, 2.0, num_heads)[:, None]
+    d = np.arange(extent)[None, :]
+    t = -a * np.log1p(d) + 0.25 * rng.standard_normal((num_heads, extent))
+    return bf16(t.astype(np.float32)).float().numpy()
+
+
 def make_attn_case(name: str, seed: int, seq_lens, q_lens, num_q_heads: int,
                    num_kv_heads: int, head_dim: int, *, qk_dist: str = "normal",
                    v_std: float = 1.0, v_outlier_frac: float = 0.0,
@@ -145,12 +157,14 @@ def make_attn_case(name: str, seed: int, seq_lens, q_lens, num_q_heads: int,
                    slopes: Optional[np.ndarray] = None, fixed_scales: Optional[dict] = None,
                    v_scale_override: Optional[float] = None, spare_frac: float = 0.25,
                    min_pool: int = 0, split_store_at_new: bool = True,
-                   softmax_scale: Optional[float] = None) -> AttnCase:
+                   softmax_scale: Optional[float] = None, rel_extent: int = 0) -> AttnCase:
     """Draw Q, K, V and a random page layout.
 
     qk_dist: "normal" for N(0,1), "rms20" for per-row RMS-normed N(0,1) scaled
     so the tensor's amax is 20. V is N(0, v_std^2) with an optional fraction of
-    outliers whose magnitude is uniform in v_outlier_range.
+    outliers whose magnitude is uniform in v_outlier_range. rel_extent > 0
+    adds a learned relative-bias table (see rel_bias_table), drawn after
+    everything else so the other draws do not depend on it.
     """
     rng = np.random.default_rng(seed)
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
@@ -178,12 +192,13 @@ def make_attn_case(name: str, seed: int, seq_lens, q_lens, num_q_heads: int,
     batches = [b for b in batches if b.size]
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(head_dim)
+    rel = rel_bias_table(rng, num_q_heads, rel_extent) if rel_extent > 0 else None
     return AttnCase(
         name=name, seed=seed, seq_lens=seq_lens, q_lens=q_lens, num_q_heads=num_q_heads,
         num_kv_heads=num_kv_heads, head_dim=head_dim, page_size=PAGE_SIZE,
         num_pages=num_pages, block_table=bt, slot_mapping=slot, seq_of_token=seq_of,
         pos_of_token=pos_of, q=bf16(q), k=bf16(k), v=bf16(v), store_batches=batches,
-        window=window, slopes=slopes, softmax_scale=float(softmax_scale),
+        window=window, slopes=slopes, rel=rel, softmax_scale=float(softmax_scale),
         fixed_scales=fixed_scales, v_scale_override=v_scale_override,
         notes={"v_outliers": n_out},
     )
