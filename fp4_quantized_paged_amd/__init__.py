@@ -39,10 +39,10 @@ class CacheDesc(ctypes.Structure):
 
 class AttnParams(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("window", ctypes.c_int32),
-                ("num_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("num_splits", ctypes.c_int32), ("rel_extent", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("q_scale", ctypes.c_float),
                 ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
-                ("alibi_slopes", ctypes.c_void_p)]
+                ("alibi_slopes", ctypes.c_void_p), ("rel_bias", ctypes.c_void_p)]
 
 
 _lib = None
@@ -181,9 +181,14 @@ def calibrate_amax(x: torch.Tensor, slot_mapping: Optional[torch.Tensor] = None,
     return amax, scale
 
 
-def _params(num_q_heads, softmax_scale, q_scale, k_scale, v_scale, window, slopes, num_splits):
-    return AttnParams(int(num_q_heads), int(window), int(num_splits), 0, float(softmax_scale),
-                      float(q_scale), float(k_scale), float(v_scale), _ptr(slopes))
+def _params(num_q_heads, softmax_scale, q_scale, k_scale, v_scale, window, slopes, num_splits,
+            rel_bias=None):
+    if rel_bias is not None:
+        assert rel_bias.dtype == torch.bfloat16 and rel_bias.is_contiguous() and rel_bias.dim() == 2
+        assert rel_bias.shape[0] == num_q_heads
+    extent = 0 if rel_bias is None else int(rel_bias.shape[1])
+    return AttnParams(int(num_q_heads), int(window), int(num_splits), extent, float(softmax_scale),
+                      float(q_scale), float(k_scale), float(v_scale), _ptr(slopes), _ptr(rel_bias))
 
 
 def decode_workspace_bytes(cache, num_seqs: int, max_seq_len: int, num_q_heads: int,
@@ -198,9 +203,11 @@ def decode(cache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Te
            max_seq_len: int, softmax_scale: float, q_scale: float = 1.0, k_scale: float = 1.0,
            v_scale: float = 1.0, window: int = 0, slopes: Optional[torch.Tensor] = None,
            num_splits: int = 0, out: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """kvq_paged_attn_decode. q bf16 [B, Hq, Dqk] -> out bf16 [B, Hq, Dv]."""
-    _need_cuda(q, block_table, seq_lens, slopes)
+           workspace: Optional[torch.Tensor] = None,
+           rel_bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """kvq_paged_attn_decode. q bf16 [B, Hq, Dqk] -> out bf16 [B, Hq, Dv].
+    rel_bias: learned relative-bias table, bf16 [Hq, extent]."""
+    _need_cuda(q, block_table, seq_lens, slopes, rel_bias)
     assert q.dtype == torch.bfloat16 and q.is_contiguous()
     assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
     B, Hq, _ = q.shape
@@ -208,7 +215,7 @@ def decode(cache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Te
     dv = 512 if d.format == FMT_NVFP4_MLA368 else d.head_dim
     if out is None:
         out = torch.empty((B, Hq, dv), dtype=torch.bfloat16, device=q.device)
-    p = _params(Hq, softmax_scale, q_scale, k_scale, v_scale, window, slopes, num_splits)
+    p = _params(Hq, softmax_scale, q_scale, k_scale, v_scale, window, slopes, num_splits, rel_bias)
     need = int(lib().kvq_decode_workspace_bytes(ctypes.byref(d), B, int(max_seq_len), ctypes.byref(p)))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -225,15 +232,16 @@ def prefill(cache, q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,
             block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
             softmax_scale: float, q_scale: float = 1.0, k_scale: float = 1.0,
             v_scale: float = 1.0, window: int = 0, slopes: Optional[torch.Tensor] = None,
-            out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """kvq_paged_attn_prefill. q bf16 [sumQ, Hq, D] -> out bf16 [sumQ, Hq, D]."""
-    _need_cuda(q, cu_q_lens, block_table, seq_lens, slopes)
+            out: Optional[torch.Tensor] = None, rel_bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """kvq_paged_attn_prefill. q bf16 [sumQ, Hq, D] -> out bf16 [sumQ, Hq, D].
+    rel_bias: learned relative-bias table, bf16 [Hq, extent]."""
+    _need_cuda(q, cu_q_lens, block_table, seq_lens, slopes, rel_bias)
     assert q.dtype == torch.bfloat16 and q.is_contiguous()
     total_q, Hq, D = q.shape
     d = cache.desc
     if out is None:
         out = torch.empty((total_q, Hq, D), dtype=torch.bfloat16, device=q.device)
-    p = _params(Hq, softmax_scale, q_scale, k_scale, v_scale, window, slopes, 0)
+    p = _params(Hq, softmax_scale, q_scale, k_scale, v_scale, window, slopes, 0, rel_bias)
     st = lib().kvq_paged_attn_prefill(ctypes.byref(d), _ptr(q), _ptr(cu_q_lens), total_q,
                                       int(max_q_len), _ptr(block_table), block_table.stride(0),
                                       _ptr(seq_lens), int(seq_lens.shape[0]), int(max_seq_len),

@@ -3,8 +3,11 @@
 // What is computed (vLLM PR 54705, "Purpose", query-quantization and
 // descale-handling bullets): Q is quantized to e4m3 with its per-tensor scale;
 // raw scores are e4m3 dot products; the QK descale is folded into the softmax
-// scale and the exact bf16 relative bias is added after it; the V descale
-// multiplies the output. Online softmax across key blocks follows the
+// scale and the exact bf16 relative bias is added after it (bf16(slope_h *
+// -(p - j)), or the entry T[h][min(p - j, E - 1)] of a learned table: the
+// page's "Environment" and "Test Plan" sections, extents 128 and 1024; blocks
+// entirely beyond the extent add the last entry without lookups); the V
+// descale multiplies the output. Online softmax across key blocks follows the
 // evidence document's "Tier 0" (P in fp8, pre-scaled by 2^8 so its largest
 // value 256 stays below the e4m3 maximum; rescaling is exact here, i.e. a
 // threshold of 0).
@@ -122,7 +125,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
   }
   const float slope = (a.slopes != nullptr && qvalid) ? a.slopes[head] : 0.0f;
-  const bool has_bias = a.slopes != nullptr;
+  // learned table: this head's row; distances from rel_extent - 1 on read
+  // its last entry (kept pre-multiplied by log2(e) for the far blocks)
+  const uint16_t *rel_row = a.rel != nullptr ? a.rel + (size_t)head * a.rel_extent : nullptr;
+  const float rel_last = rel_row != nullptr ? __uint_as_float((uint32_t)rel_row[a.rel_extent - 1] << 16) * kLog2e : 0.0f;
+  const bool has_bias = a.slopes != nullptr || a.rel != nullptr;
   const float qpos = (float)(L - 1);
 
   float m_run = -INFINITY;   // running max, log2 domain
@@ -236,7 +243,26 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 
     // ---- scores in the log2 domain: x = raw * fold (+ bias); masked keys -inf
     const int kpos0 = vp0 * 16;   // absolute position of this lane's first key
-    if (has_bias) {
+    if (rel_row != nullptr) {
+      // keys of this block sit at distances L - 1 - kpos; a block whose
+      // nearest key is at least rel_extent - 1 away reads only the last entry
+      if ((L - 1) - (pbase * 16 + 127) >= a.rel_extent - 1) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sacc[j][i] = fmaf(sacc[j][i], a.fold_log2, rel_last);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kpos = kpos0 + 16 * (j >> 2) + 4 * (j & 3) + i;
+            const int e = min(max((L - 1) - kpos, 0), a.rel_extent - 1);   // later keys are masked
+            const float bias = __uint_as_float((uint32_t)rel_row[e] << 16);
+            sacc[j][i] = fmaf(sacc[j][i], a.fold_log2, bias * kLog2e);
+          }
+      }
+    } else if (has_bias) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
 #pragma unroll

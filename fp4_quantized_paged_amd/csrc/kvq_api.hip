@@ -51,10 +51,19 @@ int check_cache(const kvq_cache *c) {
 int check_params(const kvq_cache *c, const kvq_attn_params *p) {
   if (p == nullptr) return KVQ_ERR_INVALID_ARG;
   if (p->num_q_heads <= 0 || p->num_q_heads % c->num_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
-  if (p->window < 0 || p->num_splits < 0 || p->reserved != 0) return KVQ_ERR_INVALID_ARG;
+  if (p->window < 0 || p->num_splits < 0) return KVQ_ERR_INVALID_ARG;
+  if (p->rel_bias != nullptr) {
+    if (p->rel_extent < 1 || p->rel_extent > (1 << 20) || p->alibi_slopes != nullptr ||
+        (reinterpret_cast<uintptr_t>(p->rel_bias) & 1) != 0)
+      return KVQ_ERR_INVALID_ARG;
+  } else if (p->rel_extent != 0) {
+    return KVQ_ERR_INVALID_ARG;
+  }
   if (!good_scale(p->softmax_scale) || !good_scale(p->k_scale)) return KVQ_ERR_BAD_SCALE;
   if (c->format == KVQ_FMT_E4M3 && (!good_scale(p->q_scale) || !good_scale(p->v_scale)))
     return KVQ_ERR_BAD_SCALE;
+  if (c->format != KVQ_FMT_E4M3 && (p->window != 0 || p->alibi_slopes != nullptr || p->rel_bias != nullptr))
+    return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 
@@ -239,6 +248,8 @@ int kvq_paged_attn_decode(const kvq_cache *cache, const void *q, const int32_t *
     a.bt_stride = block_table_stride;
     a.seq_lens = seq_lens;
     a.slopes = params->alibi_slopes;
+    a.rel = params->rel_bias;
+    a.rel_extent = params->rel_extent;
     a.out = static_cast<uint16_t *>(out);
     a.part_o = static_cast<float *>(workspace);
     a.part_ml = pl.workspace > 0
@@ -305,6 +316,8 @@ int kvq_paged_attn_prefill(const kvq_cache *cache, const void *q, const int32_t 
   a.bt_stride = block_table_stride;
   a.seq_lens = seq_lens;
   a.slopes = params->alibi_slopes;
+  a.rel = params->rel_bias;
+  a.rel_extent = params->rel_extent;
   a.out = static_cast<uint16_t *>(out);
   a.batch = num_seqs;
   a.hq = params->num_q_heads;

@@ -53,6 +53,8 @@ struct DecodeE4M3Launch {
   int64_t bt_stride;
   const int32_t *seq_lens;
   const float *slopes;         // [Hq] or nullptr
+  const uint16_t *rel;         // bf16 [Hq][rel_extent] or nullptr
+  int rel_extent;
   uint16_t *out;               // [B][Hq][D]
   float *part_o;               // [B][Hq][S][D]
   float *part_ml;              // [B][Hq][S][2]
@@ -70,7 +72,9 @@ struct PrefillE4M3Launch {
   const int32_t *block_table;
   int64_t bt_stride;
   const int32_t *seq_lens;
-  const float *slopes;
+  const float *slopes;         // [Hq] or nullptr
+  const uint16_t *rel;         // bf16 [Hq][rel_extent] or nullptr
+  int rel_extent;
   uint16_t *out;
   int batch, hq, hkv, d, window, max_q_len;
   float q_inv, fold_log2, v_scale;

@@ -66,7 +66,9 @@ constexpr int kXchOff = kWaves * 2 * kKtBytes;
 constexpr int kXchBytes = kPairs * 2 * 2 * 64 * 16;
 constexpr int kSmemBytes = kXchOff + kXchBytes;
 static_assert(2 * 2 * kHeads * kSlabRow * 4 <= kXchOff, "merge slabs fit");
-static_assert(kHeads * kStageRowU4 * 16 <= kXchOff, "staged Q fits");
+static_assert(((kHeads * (kLat + 64) / 8 + kThreads - 1) / kThreads * kThreads / ((kLat + 64) / 8) + 1) *
+                  kStageRowU4 * 16 <= kXchOff,
+              "staged Q, with the prologue's spill-over rows, fits");
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
@@ -154,10 +156,45 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   const int npages = (L + 15) >> 4;
   const int p_begin = split * pages_per_split;
   const int p_end = min(npages, p_begin + pages_per_split);
+  const int32_t *bt = a.block_table + (size_t)b * a.bt_stride;
+  const int nbt = p_end - p_begin;   // at most kMaxSplitPages = kThreads
+  // Page ids first (clamped indexes keep the loads unconditional): this
+  // wave's copy of the split's first 64, and the split's block-table slice
+  // (one entry per thread).
+  const int btw = bt[p_begin + max(0, min(lane, nbt - 1))];
+  const int btt = bt[p_begin + max(0, min((int)threadIdx.x, nbt - 1))];
+  __builtin_amdgcn_sched_barrier(0);
+
+  // coalesced page loads: nibble load i, lane l -> key 8i + l/8, bytes
+  // 128*half + 16*(l%8); chunk load, lane l -> key l/4, chunk l%4 of
+  // {scales 256 + 16*half, s2 block 288, RoPE 304 + 32*half, +16}
+  const uint32_t off_nib = (lane >> 3) * kRec + 128 * half + 16 * (lane & 7);
+  const int tch = lane & 3;
+  const uint32_t off_tail = (lane >> 2) * kRec + (tch == 0 ? 256 + 16 * half : (tch == 1 ? 288 : 304 + 32 * half + 16 * (tch - 2)));
+  // Every page slot issues the same five loads, so the wait for one buffer
+  // never covers the later buffers' loads in flight. Without a page to fetch
+  // they read this sequence's Q block instead (18 KB, read anyway, unused).
+  const uint8_t *dummy = (const uint8_t *)(a.q + (size_t)b * a.hq * (kLat + 64));
+  auto fetch_from = [&](const uint8_t *page, PageRaw &r) {
+    r.nib[0] = __builtin_nontemporal_load((const v4u *)(page + off_nib));
+    r.nib[1] = __builtin_nontemporal_load((const v4u *)(page + off_nib + 8 * kRec));
+    r.tail = __builtin_nontemporal_load((const v4u *)(page + off_tail));
+  };
+  // The first four page slots are requested before the Q work (page ids
+  // from the wave's own copy), so that their latency overlaps Q's.
+  PageRaw buf0, buf1, buf2, buf3;
   {
-    const int32_t *bt = a.block_table + (size_t)b * a.bt_stride;
-    for (int i = threadIdx.x; i < p_end - p_begin; i += kThreads) s_bt[i] = bt[p_begin + i];
+    auto first = [&](int k, PageRaw &r) {
+      const int p = p_begin + pair + k * kPairs;
+      const int ph = __builtin_amdgcn_readlane(btw, pair + k * kPairs);   // a clamped copy past the split
+      fetch_from(p < p_end ? a.records + (size_t)ph * (16 * kRec) : dummy, r);
+    };
+    first(0, buf0);
+    first(1, buf1);
+    first(2, buf2);
+    first(3, buf3);
   }
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- Q: stage bf16 in LDS, find each head's power-of-two scale k (largest
   // element of head h times 2^k in [2^13, 2^14)), keep this lane's operands
@@ -165,11 +202,22 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   // 512 + 32*half + 8*grp) as fp16 Q * 2^k in registers
   uint4 qop[8], qrope;
   {
-    uint4 *qs = (uint4 *)smem;
+    // Q is requested behind the first pages, so both arrive in one round trip
+    constexpr int kQU4 = kHeads * (kLat + 64) / 8;
     const uint4 *qsrc = (const uint4 *)(a.q + (size_t)b * a.hq * (kLat + 64));
-    for (int c = threadIdx.x; c < kHeads * (kLat + 64) / 8; c += kThreads) {
+    uint4 qv[(kQU4 + kThreads - 1) / kThreads];
+#pragma unroll
+    for (int j = 0; j < (kQU4 + kThreads - 1) / kThreads; ++j)
+      qv[j] = qsrc[min((int)threadIdx.x + j * kThreads, kQU4 - 1)];
+    if ((int)threadIdx.x < nbt) s_bt[threadIdx.x] = btt;
+    uint4 *qs = (uint4 *)smem;
+    // unconditional stores: entries past Q (rows 16 .. 21) land in K-row
+    // buffer space that is cleared below
+#pragma unroll
+    for (int j = 0; j < (kQU4 + kThreads - 1) / kThreads; ++j) {
+      const int c = threadIdx.x + j * kThreads;
       const int h = c / ((kLat + 64) / 8);
-      qs[h * kStageRowU4 + (c - h * ((kLat + 64) / 8))] = qsrc[c];
+      qs[h * kStageRowU4 + (c - h * ((kLat + 64) / 8))] = qv[j];
     }
     __syncthreads();
     if (wave == 0) {
@@ -223,27 +271,14 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   const int rc1 = (row & 3) >> 1;
   const uint8_t *rbase = kt + 256 * rc1 + 16 * ((4 * grp + (row >> 2)) ^ (4 * rc1)) + 8 * (row & 1);
   v4f *xch = (v4f *)(smem + kXchOff) + pair * 2 * 2 * 64;   // [buf][half][lane]
-  // coalesced page loads: nibble load i, lane l -> key 8i + l/8, bytes
-  // 128*half + 16*(l%8); chunk load, lane l -> key l/4, chunk l%4 of
-  // {scales 256 + 16*half, s2 block 288, RoPE 304 + 32*half, +16}
-  const uint32_t off_nib = (lane >> 3) * kRec + 128 * half + 16 * (lane & 7);
-  const int tch = lane & 3;
-  const uint32_t off_tail = (lane >> 2) * kRec + (tch == 0 ? 256 + 16 * half : (tch == 1 ? 288 : 304 + 32 * half + 16 * (tch - 2)));
   uint8_t *st_nib = kt + kStageNib * (lane >> 3) + 16 * (lane & 7);          // + 8*kStageNib for load 1
   uint8_t *st_tail = kt + kStageTail + kStageTailRow * (lane >> 2) + 16 * tch;
   const uint8_t *ld_nib = kt + kStageNib * row + 32 * grp;
   const uint8_t *ld_tail = kt + kStageTail + kStageTailRow * row;
 
-  // Every page slot issues the same five loads, so the wait for one buffer
-  // never covers the later buffers' loads in flight. Without a page to fetch
-  // they read this sequence's Q block instead (18 KB, just read, unused).
-  const uint8_t *dummy = (const uint8_t *)(a.q + (size_t)b * a.hq * (kLat + 64));
   auto fetch = [&](int p, PageRaw &r) {
-    const uint8_t *page = dummy;
-    if (p < p_end) page = a.records + (size_t)__builtin_amdgcn_readfirstlane(s_bt[p - p_begin]) * (16 * kRec);
-    r.nib[0] = __builtin_nontemporal_load((const v4u *)(page + off_nib));
-    r.nib[1] = __builtin_nontemporal_load((const v4u *)(page + off_nib + 8 * kRec));
-    r.tail = __builtin_nontemporal_load((const v4u *)(page + off_tail));
+    fetch_from(p < p_end ? a.records + (size_t)__builtin_amdgcn_readfirstlane(s_bt[p - p_begin]) * (16 * kRec) : dummy,
+               r);
   };
 
   // A page's bytes to the MFMA layout through the wave's staging area in
@@ -377,11 +412,6 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   };
 
   const int iters = p_end > p_begin ? (p_end - p_begin + kPairs - 1) / kPairs : 0;
-  PageRaw buf0, buf1, buf2, buf3;
-  fetch(p_begin + pair, buf0);
-  fetch(p_begin + pair + kPairs, buf1);
-  fetch(p_begin + pair + 2 * kPairs, buf2);
-  fetch(p_begin + pair + 3 * kPairs, buf3);
   PageOp op;
   stage(buf0, 0, op);   // slot 0 into K-row buffer 0
   fetch(p_begin + pair + kBufs * kPairs, buf0);

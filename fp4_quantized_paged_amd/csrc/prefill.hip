@@ -5,9 +5,11 @@
 // once: query i of a sequence with Lq new tokens and L keys sits at position
 // L - Lq + i and attends keys j <= position (and > position - window); the
 // QK descale is folded into the softmax scale and the exact bf16 relative bias
-// bf16(slope_h * -(p - j)) is added after it; the V descale multiplies the
-// output. The evidence document's "Tier 1" chunked-prefill case is the shape
-// this serves.
+// is added after it: bf16(slope_h * -(p - j)), or the entry
+// T[h][min(p - j, E - 1)] of a learned table (the page's "Environment" and
+// "Test Plan": a learned relative position bias, extents 128 and 1024); the V
+// descale multiplies the output. The evidence document's "Tier 1"
+// chunked-prefill case is the shape this serves.
 //
 // Kernel design (gfx950, wave64, 8 waves per workgroup):
 //  * a workgroup owns 32 consecutive new tokens of one sequence and up to 8
@@ -26,7 +28,9 @@
 //    accumulates the row sums of the rounded P, so the normaliser matches
 //    what PV summed;
 //  * the bf16 bias of a block takes at most 159 distinct distances per head;
-//    each wave fills a small LDS table of them and looks the scores' bias up;
+//    each wave fills a small LDS table of them (from the slope or from the
+//    learned table) and looks the scores' bias up; with the learned table, a
+//    block entirely beyond its extent adds the last entry instead;
 //  * workgroups are numbered so that all tiles of one (sequence, KV head) land
 //    on the same XCD (dispatch is round-robin over the 8 XCDs), where they
 //    stream the same K/V blocks through that XCD's L2.
@@ -80,7 +84,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
-template <bool kBias>
+// Bias kinds: none, per-head slopes bf16(slope * -d), learned table T[h][min(d, E - 1)].
+constexpr int kBiasNone = 0, kBiasSlope = 1, kBiasTable = 2;
+
+template <int kKind>
 __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blocks) {
   __shared__ PrefillSmem sm;
@@ -134,7 +141,10 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
       }
     }
   }
-  const float slope = kBias ? a.slopes[head] : 0.0f;
+  constexpr bool kBias = kKind != kBiasNone;
+  const float slope = kKind == kBiasSlope ? a.slopes[head] : 0.0f;
+  const uint16_t *rel_row = kKind == kBiasTable ? a.rel + (size_t)head * a.rel_extent : nullptr;
+  const float rel_last = kKind == kBiasTable ? __uint_as_float((uint32_t)rel_row[a.rel_extent - 1] << 16) * kLog2e : 0.0f;
 
   float m_run[2] = {-INFINITY, -INFINITY};
   v4f o[2][8];
@@ -217,11 +227,20 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
     const int j0 = blk * kBlkKeys;
 
     // ---- per-wave bias table for this block: entry e <-> distance
-    // d = (P0 - j0) + e - 127, value bf16(slope * -d) * log2(e)
-    if (kBias) {
+    // d = (P0 - j0) + e - 127, value bf16(slope * -d) or T[min(d, E - 1)],
+    // times log2(e). With the learned table, a block whose nearest key is at
+    // least E - 1 from the tile's first query reads only the table's last
+    // entry (no lookups, no table).
+    const bool far = kKind == kBiasTable && P0 - (j0 + kBlkKeys - 1) >= a.rel_extent - 1;
+    if (kBias && !far) {
       for (int e = lane; e < kBiasN; e += 64) {
-        const float d = (float)(P0 - j0 + e - 127);
-        sm.bias[wave][e] = round_bf16_finite(slope * -d) * kLog2e;
+        if (kKind == kBiasSlope) {
+          const float d = (float)(P0 - j0 + e - 127);
+          sm.bias[wave][e] = round_bf16_finite(slope * -d) * kLog2e;
+        } else {
+          const int d = min(max(P0 - j0 + e - 127, 0), a.rel_extent - 1);   // later keys are masked
+          sm.bias[wave][e] = __uint_as_float((uint32_t)rel_row[d] << 16) * kLog2e;
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -253,7 +272,12 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
       const float *tb = &sm.bias[wave][r - 32 * grp + 96];
       const int c_hi = P0 + r - j0 - 32 * grp;              // keys with c <= c_hi are causal
       const int c_lo = a.window > 0 ? c_hi - a.window : -1;  // and c > c_lo inside the window
-      if (kBias) {
+      if (kBias && far) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[cb][j][i] = fmaf(s[cb][j][i], fold, rel_last);
+      } else if (kBias) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -346,10 +370,13 @@ hipError_t launch_prefill_e4m3(const PrefillE4M3Launch &a, hipStream_t s) {
   if (tiles == 0) return hipSuccess;
   const size_t grid = (size_t)8 * ((units + 7) / 8) * tiles;
   if (a.slopes != nullptr)
-    hipLaunchKernelGGL(prefill_e4m3_kernel<true>, dim3((unsigned)grid), dim3(64 * kPW), 0, s, a, tiles, units,
+    hipLaunchKernelGGL(prefill_e4m3_kernel<kBiasSlope>, dim3((unsigned)grid), dim3(64 * kPW), 0, s, a, tiles, units,
+                       head_blocks);
+  else if (a.rel != nullptr)
+    hipLaunchKernelGGL(prefill_e4m3_kernel<kBiasTable>, dim3((unsigned)grid), dim3(64 * kPW), 0, s, a, tiles, units,
                        head_blocks);
   else
-    hipLaunchKernelGGL(prefill_e4m3_kernel<false>, dim3((unsigned)grid), dim3(64 * kPW), 0, s, a, tiles, units,
+    hipLaunchKernelGGL(prefill_e4m3_kernel<kBiasNone>, dim3((unsigned)grid), dim3(64 * kPW), 0, s, a, tiles, units,
                        head_blocks);
   return hipGetLastError();
 }

@@ -105,7 +105,8 @@ typedef struct {
                             KV splits per (sequence, KV head) in decode. The
                             library clamps it: at least 4 pages per split,
                             and for NVFP4 at most 512 pages per split */
-  int32_t reserved;      /* must be 0 */
+  int32_t rel_extent;    /* entries per head of rel_bias, 1 .. 1,048,576,
+                            when rel_bias is set; 0 otherwise */
   float softmax_scale;   /* finite, > 0 */
   float q_scale;         /* E4M3: Q quantization scale; NVFP4: ignored */
   float k_scale;         /* E4M3: K descale; NVFP4: RoPE descale */
@@ -113,6 +114,13 @@ typedef struct {
   const float *alibi_slopes; /* device fp32 [num_q_heads] or NULL: additive
                             bias bf16(slope_h * -(p - j)) added after the
                             descaled QK^T, [PR54705] "Purpose", descale bullet */
+  const uint16_t *rel_bias; /* device bf16 [num_q_heads][rel_extent] or NULL:
+                            learned relative bias ([PR54705] "Environment":
+                            the model's learned relative position bias;
+                            "Test Plan": extents 128 and 1024),
+                            bias(h, p, j) = rel_bias[h][min(p - j, rel_extent - 1)]
+                            added where the slope bias is. At most one of
+                            alibi_slopes and rel_bias may be set. */
 } kvq_attn_params;
 
 /*
@@ -174,8 +182,9 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t num_seqs,
  * KVQ_FMT_NVFP4_MLA368 ([PR189]): q bf16 [num_seqs][num_q_heads][576], not
  *   quantized; K = [latent ; RoPE] decoded from the records (latent =
  *   e2m1 * group scale * record outer scale, RoPE = e4m3 * k_scale), V =
- *   latent; out bf16 [num_seqs][num_q_heads][512]. num_q_heads must be 16 and
- *   max_seq_len at most 524,288 (KVQ_ERR_UNSUPPORTED otherwise).
+ *   latent; out bf16 [num_seqs][num_q_heads][512]. num_q_heads must be 16,
+ *   max_seq_len at most 524,288, window 0 and both biases NULL
+ *   (KVQ_ERR_UNSUPPORTED otherwise).
  *
  * block_table: device int32 [num_seqs][block_table_stride], pages of each
  * sequence in order. seq_lens: device int32 [num_seqs]. max_seq_len: a host

@@ -48,6 +48,7 @@ class DeviceCase:
         self.seq_lens = torch.from_numpy(case.seq_lens).to(device)
         self.cu_q_lens = torch.from_numpy(case.cu_q_lens).to(device)
         self.slopes = None if case.slopes is None else torch.from_numpy(case.slopes).to(device)
+        self.rel = None if case.rel is None else torch.from_numpy(case.rel).to(torch.bfloat16).to(device)
 
     def calibrate(self):
         """GPU amax/448 scales (read back once, as a caller would)."""
@@ -72,13 +73,13 @@ class DeviceCase:
         c = self.case
         return kvq.decode(self.cache, self.q, self.block_table, self.seq_lens, c.max_seq_len,
                           c.softmax_scale, scales["q"], scales["k"], scales["v"], c.window,
-                          self.slopes, **kw)
+                          self.slopes, rel_bias=self.rel, **kw)
 
     def prefill(self, scales, **kw):
         c = self.case
         return kvq.prefill(self.cache, self.q, self.cu_q_lens, c.max_q_len, self.block_table,
                            self.seq_lens, c.max_seq_len, c.softmax_scale, scales["q"],
-                           scales["k"], scales["v"], c.window, self.slopes, **kw)
+                           scales["k"], scales["v"], c.window, self.slopes, rel_bias=self.rel, **kw)
 
 
 def oracle_scales(case):

@@ -46,12 +46,12 @@ def e4m3_desc(**kw):
 
 
 def params(**kw):
-    p = dict(num_q_heads=32, window=0, num_splits=0, reserved=0, softmax_scale=0.088,
-             q_scale=1.0, k_scale=1.0, v_scale=1.0, alibi_slopes=None)
+    p = dict(num_q_heads=32, window=0, num_splits=0, rel_extent=0, softmax_scale=0.088,
+             q_scale=1.0, k_scale=1.0, v_scale=1.0, alibi_slopes=None, rel_bias=None)
     p.update(kw)
-    return kvq.AttnParams(p["num_q_heads"], p["window"], p["num_splits"], p["reserved"],
+    return kvq.AttnParams(p["num_q_heads"], p["window"], p["num_splits"], p["rel_extent"],
                           p["softmax_scale"], p["q_scale"], p["k_scale"], p["v_scale"],
-                          p["alibi_slopes"])
+                          p["alibi_slopes"], p["rel_bias"])
 
 
 def store(lib, desc, T=4, ks=1.0, vs=1.0, k=FAKE, v=FAKE, stride=512, slot=FAKE):
@@ -100,7 +100,12 @@ def test_decode_validation(lib):
     d = e4m3_desc()
     assert decode(lib, d, params(num_q_heads=30)) == -1          # Hq % Hkv != 0
     assert decode(lib, d, params(window=-1)) == -1
-    assert decode(lib, d, params(reserved=1)) == -1
+    assert decode(lib, d, params(rel_extent=1)) == -1                # extent without a table
+    assert decode(lib, d, params(rel_bias=FAKE)) == -1               # table without an extent
+    assert decode(lib, d, params(rel_bias=FAKE, rel_extent=(1 << 20) + 1)) == -1
+    assert decode(lib, d, params(rel_bias=FAKE + 1, rel_extent=128)) == -1   # misaligned bf16
+    assert decode(lib, d, params(rel_bias=FAKE, rel_extent=128, alibi_slopes=FAKE)) == -1
+    assert decode(lib, d, params(rel_bias=FAKE, rel_extent=128), B=0) == 0
     for bad in (0.0, -2.0, math.nan, math.inf):
         assert decode(lib, d, params(softmax_scale=bad)) == -3
         assert decode(lib, d, params(q_scale=bad)) == -3
@@ -126,6 +131,10 @@ def test_nvfp4_decode_validation(lib):
     long_len = 64 * 512 * 16 + 1                                       # past 64 splits of 512 pages
     assert decode(lib, nv, params(num_q_heads=16), max_len=long_len, bt_stride=(long_len + 15) // 16) == -2
     assert decode(lib, nv, params(num_q_heads=16), B=0) == 0
+    # no window or bias on the MLA path
+    assert decode(lib, nv, params(num_q_heads=16, window=512), B=0) == -2
+    assert decode(lib, nv, params(num_q_heads=16, alibi_slopes=FAKE), B=0) == -2
+    assert decode(lib, nv, params(num_q_heads=16, rel_bias=FAKE, rel_extent=128), B=0) == -2
 
 
 def test_prefill_validation(lib):
@@ -140,3 +149,32 @@ def test_prefill_validation(lib):
     nv = kvq.CacheDesc(2, 16, 1, 576, 64, FAKE, None)
     assert f(ctypes.byref(nv), FAKE, FAKE, 10, 5, FAKE, 64, FAKE, 2, 100, ctypes.byref(params(num_q_heads=16)),
              FAKE, None, 0, None) == -2
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """The ctypes mirrors of kvq_cache and kvq_attn_params have the header's
+    field offsets and sizes (checked by compiling offsetof/sizeof with gcc)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    structs = {"kvq_cache": kvq.CacheDesc, "kvq_attn_params": kvq.AttnParams}
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "kvq.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append('  printf("%s size %%zu\\n", sizeof(%s));' % (cname, cname))
+        for fname, _ in cls._fields_:
+            lines.append('  printf("%s %s %%zu\\n", offsetof(%s, %s));' % (cname, fname, cname, fname))
+    lines.append("  return 0;\n}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-std=c11", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        cname, field, val = line.split()
+        got[(cname, field)] = int(val)
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for fname, _ in cls._fields_:
+            assert got[(cname, fname)] == getattr(cls, fname).offset, (cname, fname)

@@ -23,7 +23,7 @@ def run_case(c, seqs=None, **kw):
     tok = None if seqs is None else seq_tokens(c, seqs)
     kc, vc = oracle_cache(c, so, tokens=tok)
     ref = paged_decode(c.q.float().numpy(), kc, vc, c.block_table, c.seq_lens, c.softmax_scale,
-                       so["q"], so["k"], so["v"], c.window, c.slopes, seqs=seqs)
+                       so["q"], so["k"], so["v"], c.window, c.slopes, seqs=seqs, rel=c.rel)
     if seqs is not None:
         return dc, out[torch.tensor(seqs)], ref[seqs]
     return dc, out, ref
@@ -67,6 +67,38 @@ def test_decode_shapes(lens, hq, hkv, d, window, bias, splits):
     for b, L in enumerate(lens):
         if L == 0:
             assert torch.all(out[b] == 0)
+
+
+REL_CASES = [
+    # (seq_lens, Hq, Hkv, D, window, extent): learned relative-bias table
+    ([1, 15, 16, 17, 127, 128, 129, 1000], 8, 2, 64, 0, 128),
+    ([0, 5, 300, 2049], 32, 4, 128, 0, 1024),
+    ([5000, 511, 512, 513], 32, 4, 128, 512, 128),   # sliding window at extent 128
+    ([3000, 700], 32, 1, 128, 0, 1024),              # two query tiles
+    ([2500, 40], 12, 3, 128, 100, 1),                # extent 1: one value per head
+    ([1300, 130], 8, 2, 128, 0, 5000),               # extent past every distance
+]
+
+
+@pytest.mark.parametrize("lens,hq,hkv,d,window,extent", REL_CASES)
+@pytest.mark.parametrize("splits", [0, 3])
+def test_decode_learned_bias(lens, hq, hkv, d, window, extent, splits):
+    c = make_attn_case("rel", 300 + len(lens) + hq + d, lens, [1] * len(lens), hq, hkv, d,
+                       qk_dist="rms20", v_std=4.0, v_outlier_frac=1e-3, window=window,
+                       rel_extent=extent)
+    _, out, ref = run_case(c, num_splits=splits)
+    check_attention(out, ref, "rel %s hq%d hkv%d d%d w%d E%d" % (lens, hq, hkv, d, window, extent))
+
+
+def test_batched_decode_learned_bias_sampled():
+    """The batched-decode shape (64 x 8,192 tokens) with a 1,024-entry table."""
+    c0 = config_batched_decode()
+    c = make_attn_case("batched_decode_rel", 1, [8192] * 64, [1] * 64, 32, 4, 128,
+                       qk_dist="rms20", v_std=8.0, v_outlier_frac=1e-3, v_scale_override=3.0,
+                       split_store_at_new=False, rel_extent=1024)
+    assert torch.equal(c.k, c0.k)       # same draws as the bias-free workload
+    _, out, ref = run_case(c, seqs=[0, 33, 63])
+    print(check_attention(out, ref, "batched_decode rel1024"))
 
 
 def test_batched_decode_full_size_sampled():

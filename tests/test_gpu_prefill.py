@@ -21,7 +21,8 @@ def run_case(c, rows=None, seqs=None):
     tok = None if seqs is None else seq_tokens(c, seqs)
     kc, vc = oracle_cache(c, so, tokens=tok)
     ref = paged_prefill(c.q.float().numpy(), c.cu_q_lens, kc, vc, c.block_table, c.seq_lens,
-                        c.softmax_scale, so["q"], so["k"], so["v"], c.window, c.slopes, rows=rows)
+                        c.softmax_scale, so["q"], so["k"], so["v"], c.window, c.slopes, rows=rows,
+                        rel=c.rel)
     if rows is not None:
         return dc, out[torch.from_numpy(np.asarray(rows))], ref[rows]
     return dc, out, ref
@@ -46,6 +47,24 @@ def test_prefill_shapes(lens, qlens, hq, hkv, window, bias):
                        v_std=2.0, window=window, slopes=slopes)
     _, out, ref = run_case(c)
     print(check_attention(out, ref, "prefill %s %s hq%d hkv%d w%d" % (lens, qlens, hq, hkv, window)))
+
+
+REL_CASES = [
+    # (seq_lens, q_lens, Hq, Hkv, window, extent): learned relative-bias table
+    ([137, 64, 501], [37, 64, 1], 32, 4, 0, 128),
+    ([300, 1000], [300, 33], 16, 2, 64, 128),        # sliding window at extent 128
+    ([2600, 777], [129, 777], 8, 1, 0, 1024),         # far blocks and near blocks
+    ([260, 90], [70, 90], 12, 3, 0, 1),
+    ([900], [45], 32, 2, 0, 4096),                    # extent past every distance
+]
+
+
+@pytest.mark.parametrize("lens,qlens,hq,hkv,window,extent", REL_CASES)
+def test_prefill_learned_bias(lens, qlens, hq, hkv, window, extent):
+    c = make_attn_case("prefill_rel", 400 + sum(qlens) + hq, lens, qlens, hq, hkv, 128,
+                       v_std=2.0, window=window, rel_extent=extent)
+    _, out, ref = run_case(c)
+    print(check_attention(out, ref, "prefill rel %s %s hq%d w%d E%d" % (lens, qlens, hq, window, extent)))
 
 
 def test_chunked_prefill_full_size_sampled():
