@@ -254,10 +254,26 @@ def main():
     }
     log("decode %.2f us, %.0f GB/s (%.1f%% of peak)" % (dec_ms * 1e3, achieved,
                                                          100 * achieved / HBM_PEAK_GBPS))
+    rel_rows = {}
+    if not args.skip_extras:
+        # the same decode with a learned relative-bias table of 1,024 entries
+        from workloads import rel_bias_table
+        rel = torch.from_numpy(rel_bias_table(np.random.default_rng(5), Hq, 1024)).to(torch.bfloat16).to(dev)
+
+        def decode_rel(i):
+            kvq.decode(caches[i % 2], q, bt, seq_lens, L, c.softmax_scale, scales["q"], scales["k"],
+                       scales["v"], out=out, workspace=ws, rel_bias=rel)
+        for i in range(2):
+            decode_rel(i)
+        rms = back_to_back_ms(torch, decode_rel, args.steps)
+        rel_rows["decode_rel1024"] = {"us": round(rms * 1e3, 2),
+                                      "GB_s": round(dec_bytes / (rms * 1e-3) / 1e9, 1),
+                                      "pct_of_peak": round(100 * dec_bytes / (rms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
     del caches, k_new, v_new
 
     if not args.skip_extras:
         result["rows"] = extras(torch, kvq, c, k, v, q, slot, scales)
+        result["rows"].update(rel_rows)
     del k, v, q
     torch.cuda.empty_cache()
 
@@ -398,6 +414,12 @@ def prefill_rows(torch, kvq):
                                                slopes=slopes, out=out), reps=5)
     fl = prefill_flops(c.seq_lens, c.q_lens, c.num_q_heads, c.head_dim)
     tf = fl / (ms * 1e-3) / 1e12
+    # the same prefill with a learned relative-bias table of 1,024 entries
+    from workloads import rel_bias_table
+    rel = torch.from_numpy(rel_bias_table(np.random.default_rng(6), c.num_q_heads, 1024)).to(torch.bfloat16).to(dev)
+    ms_rel = timed_mean(torch, lambda: kvq.prefill(cache, q, cu, c.max_q_len, bt, sl, c.max_seq_len,
+                                                   c.softmax_scale, sc["q"], sc["k"], sc["v"],
+                                                   out=out, rel_bias=rel), reps=5)
     T = int(kn.shape[0])
     del cache
     torch.cuda.empty_cache()
@@ -405,6 +427,9 @@ def prefill_rows(torch, kvq):
                                 "context": c.max_seq_len, "us": round(ms * 1e3, 1),
                                 "TFLOP_s": round(tf, 1), "flops": fl,
                                 "pct_of_fp8_peak": round(100 * tf / FP8_PEAK_TFLOPS, 2)},
+            "chunked_prefill_rel1024": {"us": round(ms_rel * 1e3, 1),
+                                        "TFLOP_s": round(fl / (ms_rel * 1e-3) / 1e12, 1),
+                                        "pct_of_fp8_peak": round(100 * fl / (ms_rel * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 2)},
             "store_prefill_new": {"tokens": T, "us": round(ms_store * 1e3, 2),
                                   "tokens_per_s": round(T / (ms_store * 1e-3), 1)}}
 

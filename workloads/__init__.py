@@ -19,6 +19,7 @@ from .gen import (  # noqa: F401
     MlaCase,
     bf16,
     paged_layout,
+    rel_bias_table,
     make_attn_case,
     make_mla_case,
     config_tiny_decode,
