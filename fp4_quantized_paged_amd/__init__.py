@@ -56,6 +56,10 @@ _SIGNATURES = {
     "kvq_calibrate_amax": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p]),
+    "kvq_scale_from_amax": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_void_p]),
+    "kvq_band_counts": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]),
     "kvq_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), ctypes.c_int32,
                                                      ctypes.c_int32, ctypes.POINTER(AttnParams)]),
     "kvq_paged_attn_decode": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p,
@@ -179,6 +183,41 @@ def calibrate_amax(x: torch.Tensor, slot_mapping: Optional[torch.Tensor] = None,
                                   _ptr(slot_mapping), _ptr(amax), _ptr(scale), _stream())
     _check(st, "kvq_calibrate_amax")
     return amax, scale
+
+
+SCALE_AMAX_448, SCALE_CEIL_BF16, SCALE_SAFETY_1P3 = 0, 1, 2
+
+
+def scale_from_amax(amax: torch.Tensor, rule: int, scale: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """kvq_scale_from_amax: the scale of a running amax (1-element device fp32)
+    under one of the SCALE_* rules, as a 1-element device fp32 tensor."""
+    _need_cuda(amax)
+    assert amax.dtype == torch.float32
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=amax.device)
+    _check(lib().kvq_scale_from_amax(_ptr(amax), int(rule), _ptr(scale), _stream()), "kvq_scale_from_amax")
+    return scale
+
+
+def band_counts(x: torch.Tensor, scale: float, slot_mapping: Optional[torch.Tensor] = None,
+                counts: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """kvq_band_counts over the rows of x (bf16, first dim = rows): adds the
+    (clipped, flushed) counts at ``scale`` to ``counts`` (device int64 [2],
+    zeros when not given) and returns it."""
+    _need_cuda(x, slot_mapping)
+    assert x.dtype == torch.bfloat16
+    rows = x.shape[0]
+    row_len = 1
+    for n in x.shape[1:]:
+        row_len *= int(n)
+    x2 = x.reshape(rows, row_len)
+    if counts is None:
+        counts = torch.zeros(2, dtype=torch.int64, device=x.device)
+    assert counts.dtype == torch.int64 and counts.numel() == 2 and counts.is_contiguous()
+    st = lib().kvq_band_counts(_ptr(x2), rows, row_len, x2.stride(0) if rows else row_len,
+                               _ptr(slot_mapping), float(scale), _ptr(counts), _stream())
+    _check(st, "kvq_band_counts")
+    return counts
 
 
 def _params(num_q_heads, softmax_scale, q_scale, k_scale, v_scale, window, slopes, num_splits,

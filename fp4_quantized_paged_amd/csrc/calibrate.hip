@@ -76,6 +76,93 @@ __global__ void amax_finalize_kernel(const float *amax, float *scale) {
   if (threadIdx.x == 0) scale[0] = amax[0] / kE4M3Max;
 }
 
+// Scale rules (vLLM PR 54705 evidence "Tier 4": max(1, amax * 1.3 / 448);
+// model card "Rebuild / reproduce": ceil_to_bfloat16(amax / 448)).
+__global__ void scale_rule_kernel(const float *amax, int rule, float *scale) {
+  if (threadIdx.x != 0) return;
+  const float a = amax[0];
+  float s;
+  if (rule == 0) {
+    s = a / kE4M3Max;
+  } else if (rule == 1) {
+    uint32_t b = __float_as_uint(a / kE4M3Max);
+    if (b & 0xFFFFu) b = (b & 0xFFFF0000u) + 0x10000u;   // up to the next bf16
+    s = __uint_as_float(b);
+  } else {
+    const double t = (double)a * 1.3 / 448.0;
+    s = (float)(t > 1.0 ? t : 1.0);                        // NaN -> 1, as max(1, NaN)
+  }
+  scale[0] = s;
+}
+
+// Band counters (vLLM PR 54705 evidence "Tier 2": clip and flush-to-zero
+// counts of the stored values at a scale). Each value is decided with the
+// store's own arithmetic: y = fp32(x) * inv; clipped when |y| > 448 (the
+// clamp changes it; NaN compares false); flushed when the bf16 input is
+// nonzero and not NaN and its e4m3 code is +-0. Per-lane counts, one wave
+// and workgroup reduction, two 64-bit atomic adds per workgroup.
+__global__ __launch_bounds__(kAmaxThreads) void band_kernel(BandLaunch a) {
+  __shared__ uint32_t red[2][kAmaxWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t cpr = a.row_len >> 3;
+  const int64_t nwaves = (int64_t)gridDim.x * kAmaxWaves;
+  uint32_t n_clip = 0, n_flush = 0;
+  int64_t r = (int64_t)blockIdx.x * kAmaxWaves + wave;
+  for (; r < a.rows; r += nwaves * kRowUnroll) {
+    for (int64_t c = lane; c < cpr; c += 64) {
+      uint4 x[kRowUnroll];
+      bool keep[kRowUnroll];
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int64_t rr = r + u * nwaves;
+        keep[u] = rr < a.rows && (a.slot == nullptr || a.slot[rr] >= 0);
+        if (keep[u]) {
+          const v4u w = __builtin_nontemporal_load((const v4u *)(a.x + rr * a.row_stride + (c << 3)));
+          x[u] = make_uint4(w.x, w.y, w.z, w.w);
+        } else {
+          x[u] = make_uint4(0, 0, 0, 0);   // zeros count in neither band
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const uint32_t wd[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+        const uint2 code = quant8_e4m3(x[u], a.inv);
+        const uint32_t cw[2] = {code.x, code.y};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t h = (wd[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          const uint32_t mag = h & 0x7FFFu;
+          const float y = __uint_as_float(h << 16) * a.inv;
+          n_clip += fabsf(y) > kE4M3Max ? 1u : 0u;
+          const uint32_t cb = (cw[e >> 2] >> (8 * (e & 3))) & 0x7Fu;
+          n_flush += (mag != 0 && mag <= 0x7F80u && cb == 0) ? 1u : 0u;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    n_clip += (uint32_t)__shfl_xor((int)n_clip, off, 64);
+    n_flush += (uint32_t)__shfl_xor((int)n_flush, off, 64);
+  }
+  if (lane == 0) {
+    red[0][wave] = n_clip;
+    red[1][wave] = n_flush;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long t0 = 0, t1 = 0;
+#pragma unroll
+    for (int i = 0; i < kAmaxWaves; ++i) {
+      t0 += red[0][i];
+      t1 += red[1][i];
+    }
+    if (t0) atomicAdd(a.counts, t0);
+    if (t1) atomicAdd(a.counts + 1, t1);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_amax(const AmaxLaunch &a, int num_cus, hipStream_t s) {
@@ -92,6 +179,20 @@ hipError_t launch_amax(const AmaxLaunch &a, int num_cus, hipStream_t s) {
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+hipError_t launch_scale_rule(const float *amax, int rule, float *scale, hipStream_t s) {
+  hipLaunchKernelGGL(scale_rule_kernel, dim3(1), dim3(64), 0, s, amax, rule, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_band_counts(const BandLaunch &a, int num_cus, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  int64_t blocks = (a.rows + kAmaxWaves * kRowUnroll - 1) / (kAmaxWaves * kRowUnroll);
+  const int64_t cap = (int64_t)num_cus * 16;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(band_kernel, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace kvq

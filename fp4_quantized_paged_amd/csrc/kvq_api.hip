@@ -215,6 +215,31 @@ int kvq_calibrate_amax(const void *x, int64_t num_rows, int64_t row_len, int64_t
   return hip_status(kvq::launch_amax(a, current_cu_count(), reinterpret_cast<hipStream_t>(stream)));
 }
 
+int kvq_scale_from_amax(const float *amax, int32_t rule, float *scale_out, kvq_stream_t stream) {
+  if (amax == nullptr || scale_out == nullptr || rule < KVQ_SCALE_AMAX_448 || rule > KVQ_SCALE_SAFETY_1P3)
+    return KVQ_ERR_INVALID_ARG;
+  return hip_status(kvq::launch_scale_rule(amax, rule, scale_out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int kvq_band_counts(const void *x, int64_t num_rows, int64_t row_len, int64_t row_stride,
+                    const int64_t *slot_mapping, float scale, uint64_t *counts_inout, kvq_stream_t stream) {
+  if (counts_inout == nullptr || (reinterpret_cast<uintptr_t>(counts_inout) & 7) != 0 || num_rows < 0 ||
+      row_len <= 0 || row_len % 8 || row_stride < row_len || row_stride % 8)
+    return KVQ_ERR_INVALID_ARG;
+  if (!good_scale(scale)) return KVQ_ERR_BAD_SCALE;
+  if (num_rows == 0) return KVQ_OK;
+  if (x == nullptr || !aligned16(x)) return KVQ_ERR_INVALID_ARG;
+  kvq::BandLaunch a{};
+  a.x = static_cast<const uint16_t *>(x);
+  a.rows = num_rows;
+  a.row_len = row_len;
+  a.row_stride = row_stride;
+  a.slot = slot_mapping;
+  a.inv = 1.0f / scale;
+  a.counts = reinterpret_cast<unsigned long long *>(counts_inout);
+  return hip_status(kvq::launch_band_counts(a, current_cu_count(), reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t num_seqs, int32_t max_seq_len,
                                   const kvq_attn_params *params) {
   if (check_cache(cache) != KVQ_OK || check_params(cache, params) != KVQ_OK) return 0;

@@ -36,6 +36,16 @@ struct AmaxLaunch {
   float *scale_out;
 };
 hipError_t launch_amax(const AmaxLaunch &a, int num_cus, hipStream_t s);
+hipError_t launch_scale_rule(const float *amax, int rule, float *scale, hipStream_t s);
+
+struct BandLaunch {
+  const uint16_t *x;
+  int64_t rows, row_len, row_stride;
+  const int64_t *slot;
+  float inv;                   // fp32(1/scale), computed on the host as the store does
+  unsigned long long *counts;  // [2]: clipped, flushed
+};
+hipError_t launch_band_counts(const BandLaunch &a, int num_cus, hipStream_t s);
 
 // Split plan of the e4m3 decode kernel.
 struct DecodePlan {

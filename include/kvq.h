@@ -163,6 +163,44 @@ int kvq_calibrate_amax(const void *x, int64_t num_rows, int64_t row_len,
                        int64_t row_stride, const int64_t *slot_mapping,
                        float *amax_inout, float *scale_out, kvq_stream_t stream);
 
+/* Scale rules of kvq_scale_from_amax. */
+enum kvq_scale_rule {
+  KVQ_SCALE_AMAX_448 = 0,   /* fp32(amax) / fp32(448) ([KVcal] scale table) */
+  KVQ_SCALE_CEIL_BF16 = 1,  /* the smallest bf16 >= fp32(amax) / fp32(448),
+                               stored as fp32 ([KVcal] "Rebuild / reproduce":
+                               ceil_to_bfloat16) */
+  KVQ_SCALE_SAFETY_1P3 = 2  /* max(1, amax * 1.3 / 448) in fp64, rounded to
+                               fp32 ([PR54705] evidence "Tier 4": the
+                               calibration utility's rule) */
+};
+
+/*
+ * kvq_scale_from_amax: *scale_out = rule(*amax), computed on the device (no
+ * read-back). amax: device fp32, e.g. the running amax of
+ * kvq_calibrate_amax; scale_out: device fp32. NULL pointers or an unknown
+ * rule: KVQ_ERR_INVALID_ARG. Bit-exact: one fp32 division for the first two
+ * rules, fp64 multiply and divide for the third.
+ */
+int kvq_scale_from_amax(const float *amax, int32_t rule, float *scale_out, kvq_stream_t stream);
+
+/*
+ * kvq_band_counts: exact e4m3 band counters of the values a store at `scale`
+ * would write ([PR54705] evidence "Tier 2": clip and flush-to-zero counts of
+ * the stored values at a given scale). x, num_rows, row_len, row_stride and
+ * slot_mapping as in kvq_calibrate_amax. With y = fp32(x) * fp32(1/scale)
+ * (the store's arithmetic):
+ *   counts_inout[0] += values with |y| > 448, which the clamp changes
+ *                      (infinities counted, NaN not);
+ *   counts_inout[1] += nonzero values whose e4m3 code is +0 or -0 (NaN not).
+ * counts_inout: device uint64 [2], 8-byte aligned, accumulated across calls
+ * (the caller zeroes it to start). scale must be finite and > 0
+ * (KVQ_ERR_BAD_SCALE). Exact integer counts, independent of launch order.
+ * num_rows == 0 returns KVQ_OK without launching.
+ */
+int kvq_band_counts(const void *x, int64_t num_rows, int64_t row_len, int64_t row_stride,
+                    const int64_t *slot_mapping, float scale, uint64_t *counts_inout,
+                    kvq_stream_t stream);
+
 /*
  * Workspace (device bytes) kvq_paged_attn_decode needs for these arguments
  * on the current device. 0 means no workspace is needed. Returns 0 for

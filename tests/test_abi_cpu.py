@@ -178,3 +178,21 @@ def test_struct_layouts_match_header(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(cls), cname
         for fname, _ in cls._fields_:
             assert got[(cname, fname)] == getattr(cls, fname).offset, (cname, fname)
+
+
+def test_calibration_extras_validation(lib):
+    f = lib.kvq_scale_from_amax
+    assert f(None, 0, FAKE, None) == -1
+    assert f(FAKE, 0, None, None) == -1
+    assert f(FAKE, 3, FAKE, None) == -1          # unknown rule
+    assert f(FAKE, -1, FAKE, None) == -1
+    g = lib.kvq_band_counts
+    assert g(FAKE, 10, 512, 512, None, 1.0, None, None) == -1        # no counts buffer
+    assert g(FAKE, 10, 512, 512, None, 1.0, FAKE + 4, None) == -1    # counts not 8-byte aligned
+    assert g(FAKE, 10, 500, 512, None, 1.0, FAKE, None) == -1        # row_len % 8
+    assert g(FAKE, 10, 512, 256, None, 1.0, FAKE, None) == -1        # stride < row_len
+    for bad in (0.0, -1.0, math.nan, math.inf):
+        assert g(FAKE, 10, 512, 512, None, bad, FAKE, None) == -3
+    assert g(None, 10, 512, 512, None, 1.0, FAKE, None) == -1
+    assert g(FAKE + 2, 10, 512, 512, None, 1.0, FAKE, None) == -1    # misaligned rows
+    assert g(None, 0, 512, 512, None, 1.0, FAKE, None) == 0          # no rows: no launch

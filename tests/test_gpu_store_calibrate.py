@@ -7,6 +7,7 @@ import torch
 import fp4_quantized_paged_amd as kvq
 from oracle.codecs import bf16_bits_to_f32
 from oracle.kvcache import new_cache, store_e4m3, calibrate_amax, quantize_e4m3
+from oracle.calibration import band_counts, scale_from_amax
 from workloads import bf16, config_tiny_decode, config_batched_decode, make_attn_case
 from parity import DeviceCase, oracle_scales, oracle_cache, seq_tokens
 
@@ -181,3 +182,70 @@ def test_store_deterministic():
         kvq.store(dc.cache, dc.k, dc.v, dc.slot, 0.3, 0.7)
     torch.cuda.synchronize()
     assert torch.equal(a.cache.k, b.cache.k) and torch.equal(a.cache.v, b.cache.v)
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0, 3.0, 0.125, 20.0 / 448])
+def test_band_counts_all_bf16_patterns(scale):
+    """Clip and flush-to-zero counts over every bf16 pattern, bit-exact."""
+    x = all_patterns(4, 128).cuda()
+    got = kvq.band_counts(x, scale)
+    torch.cuda.synchronize()
+    want = band_counts(x.float().cpu().numpy(), scale)
+    assert tuple(got.cpu().tolist()) == want
+    if scale == 1.0:
+        assert want == (30528, 29952)
+
+
+def test_band_counts_slots_and_running_total():
+    rng = np.random.default_rng(8)
+    x = bf16(rng.standard_normal((300, 4, 64)).astype(np.float32) * 200.0)
+    x[::17, 0, :8] = bf16(np.full(8, 1e-5, np.float32))
+    slot = np.arange(300, dtype=np.int64)
+    slot[::3] = -1
+    xd = x.cuda()
+    counts = kvq.band_counts(xd, 1.0, torch.from_numpy(slot).cuda())
+    counts = kvq.band_counts(xd[:0], 1.0, counts=counts)            # no rows: unchanged
+    counts = kvq.band_counts(xd, 0.5, counts=counts)                # running total
+    torch.cuda.synchronize()
+    xn = x.float().numpy()
+    a = band_counts(xn, 1.0, slot)
+    b = band_counts(xn, 0.5)
+    assert tuple(counts.cpu().tolist()) == (a[0] + b[0], a[1] + b[1])
+    assert a[0] > 0 and a[1] > 0
+
+
+def test_band_counts_batched_decode_v(batched):
+    """V of the batched-decode workload (outliers up to 1,272): exact counts on
+    three sequences selected by the slot mask; over all 524,288 rows nothing
+    clips at scale 3 and the outliers clip at scale 1."""
+    c, dc = batched
+    seqs = [0, 31, 63]
+    tok = seq_tokens(c, seqs)
+    mask = np.full(c.v.shape[0], -1, np.int64)
+    mask[tok] = 0
+    vn = c.v.float().numpy()
+    for s in (1.0, 3.0):
+        got = kvq.band_counts(dc.v, s, torch.from_numpy(mask).cuda())
+        torch.cuda.synchronize()
+        assert tuple(got.cpu().tolist()) == band_counts(vn[tok], s)
+    full3 = kvq.band_counts(dc.v, 3.0)
+    full1 = kvq.band_counts(dc.v, 1.0)
+    torch.cuda.synchronize()
+    assert full3[0].item() == 0
+    assert full1[0].item() == int(np.count_nonzero(np.abs(vn) > 448))
+
+
+def test_scale_rules_match_oracle():
+    rng = np.random.default_rng(9)
+    vals = np.concatenate([[0.0, 1e-30, 448.0, 449.0, 1272.0, 812.0, 73.5, 55.8, 344.0, 345.0, 3e38],
+                           rng.lognormal(1.0, 4.0, 200)]).astype(np.float32)
+    amax = torch.from_numpy(vals).cuda()
+    for rule in (kvq.SCALE_AMAX_448, kvq.SCALE_CEIL_BF16, kvq.SCALE_SAFETY_1P3):
+        out = torch.empty_like(amax)
+        for i in range(len(vals)):
+            kvq.scale_from_amax(amax[i:i + 1], rule, out[i:i + 1])
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        want = np.array([scale_from_amax(a, rule) for a in vals], np.float32)
+        bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+        assert bad.size == 0, (rule, vals[bad[:5]], got[bad[:5]], want[bad[:5]])
