@@ -329,6 +329,12 @@ def extras(torch, kvq, c, k, v, q, slot, scales):
     ms = timed_mean(torch, lambda: (kvq.calibrate_amax(k, amax=amax), kvq.calibrate_amax(v, amax=amax)))
     cb = 2 * k.numel() * 2
     rows["calibrate_kv"] = {"us": round(ms * 1e3, 2), "GB_s": round(cb / (ms * 1e-3) / 1e9, 1)}
+    # clip / flush-to-zero band counters of K and V at their scales
+    counts = torch.zeros(2, dtype=torch.int64, device=k.device)
+    ms = timed_mean(torch, lambda: (kvq.band_counts(k, scales["k"], counts=counts),
+                                    kvq.band_counts(v, scales["v"], counts=counts)))
+    rows["band_counts_kv"] = {"us": round(ms * 1e3, 2), "GB_s": round(cb / (ms * 1e-3) / 1e9, 1),
+                              "pct_of_peak": round(100 * cb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
     del cache
     torch.cuda.empty_cache()
     rows.update(long_context_rows(torch, kvq))
