@@ -42,10 +42,14 @@ class AttnParams(ctypes.Structure):
                 ("num_splits", ctypes.c_int32), ("rel_extent", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("q_scale", ctypes.c_float),
                 ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
-                ("alibi_slopes", ctypes.c_void_p), ("rel_bias", ctypes.c_void_p)]
+                ("alibi_slopes", ctypes.c_void_p), ("rel_bias", ctypes.c_void_p),
+                ("flags", ctypes.c_uint32)]
+
+FLAG_PREFILL_FP8_P = 1
 
 
 _lib = None
+ABI_VERSION = 2   # KVQ_ABI_VERSION of include/kvq.h
 
 _SIGNATURES = {
     "kvq_abi_version": (ctypes.c_int, []),
@@ -88,6 +92,9 @@ def lib() -> ctypes.CDLL:
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args
+        if handle.kvq_abi_version() != ABI_VERSION:
+            raise RuntimeError("%s has ABI version %d, this binding expects %d: rebuild it"
+                               % (LIB_PATH, handle.kvq_abi_version(), ABI_VERSION))
         _lib = handle
     return _lib
 
@@ -221,13 +228,14 @@ def band_counts(x: torch.Tensor, scale: float, slot_mapping: Optional[torch.Tens
 
 
 def _params(num_q_heads, softmax_scale, q_scale, k_scale, v_scale, window, slopes, num_splits,
-            rel_bias=None):
+            rel_bias=None, flags=0):
     if rel_bias is not None:
         assert rel_bias.dtype == torch.bfloat16 and rel_bias.is_contiguous() and rel_bias.dim() == 2
         assert rel_bias.shape[0] == num_q_heads
     extent = 0 if rel_bias is None else int(rel_bias.shape[1])
     return AttnParams(int(num_q_heads), int(window), int(num_splits), extent, float(softmax_scale),
-                      float(q_scale), float(k_scale), float(v_scale), _ptr(slopes), _ptr(rel_bias))
+                      float(q_scale), float(k_scale), float(v_scale), _ptr(slopes), _ptr(rel_bias),
+                      int(flags))
 
 
 def decode_workspace_bytes(cache, num_seqs: int, max_seq_len: int, num_q_heads: int,
@@ -271,16 +279,19 @@ def prefill(cache, q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,
             block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
             softmax_scale: float, q_scale: float = 1.0, k_scale: float = 1.0,
             v_scale: float = 1.0, window: int = 0, slopes: Optional[torch.Tensor] = None,
-            out: Optional[torch.Tensor] = None, rel_bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+            out: Optional[torch.Tensor] = None, rel_bias: Optional[torch.Tensor] = None,
+            fp8_p: bool = False) -> torch.Tensor:
     """kvq_paged_attn_prefill. q bf16 [sumQ, Hq, D] -> out bf16 [sumQ, Hq, D].
-    rel_bias: learned relative-bias table, bf16 [Hq, extent]."""
+    rel_bias: learned relative-bias table, bf16 [Hq, extent]. fp8_p: the
+    single-term e4m3 P speed variant (KVQ_FLAG_PREFILL_FP8_P)."""
     _need_cuda(q, cu_q_lens, block_table, seq_lens, slopes, rel_bias)
     assert q.dtype == torch.bfloat16 and q.is_contiguous()
     total_q, Hq, D = q.shape
     d = cache.desc
     if out is None:
         out = torch.empty((total_q, Hq, D), dtype=torch.bfloat16, device=q.device)
-    p = _params(Hq, softmax_scale, q_scale, k_scale, v_scale, window, slopes, 0, rel_bias)
+    p = _params(Hq, softmax_scale, q_scale, k_scale, v_scale, window, slopes, 0, rel_bias,
+                FLAG_PREFILL_FP8_P if fp8_p else 0)
     st = lib().kvq_paged_attn_prefill(ctypes.byref(d), _ptr(q), _ptr(cu_q_lens), total_q,
                                       int(max_q_len), _ptr(block_table), block_table.stride(0),
                                       _ptr(seq_lens), int(seq_lens.shape[0]), int(max_seq_len),

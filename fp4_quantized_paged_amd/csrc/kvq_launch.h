@@ -87,6 +87,7 @@ struct PrefillE4M3Launch {
   int rel_extent;
   uint16_t *out;
   int batch, hq, hkv, d, window, max_q_len;
+  int fp8_p;                   // single-term e4m3 P with lazy rescale (opt-in variant)
   float q_inv, fold_log2, v_scale;
 };
 hipError_t launch_prefill_e4m3(const PrefillE4M3Launch &a, hipStream_t s);

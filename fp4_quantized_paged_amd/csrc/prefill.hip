@@ -61,7 +61,9 @@ __device__ __forceinline__ int kswz(int kidx) {
 
 struct __align__(16) PrefillSmem {
   uint4 k[kKBytes / 16];        // [128 keys][8 chunks of 16 B], chunk c at slot c ^ kswz(key)
-  uint4 v[2 * kVBytes / 16];    // bf16 V^T: [8 pages][2 halves][128 dims][8 tokens]
+  uint4 v[2 * kVBytes / 16];    // bf16 V^T: [8 pages][2 halves][128 dims][8 tokens];
+                                // fp8-P variant: e4m3 V^T [8 pages][128 dims][16 tokens]
+                                // in the first half
   float bias[kPW][kBiasN];      // per wave: bias * log2(e) by distance
 };
 
@@ -87,7 +89,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Bias kinds: none, per-head slopes bf16(slope * -d), learned table T[h][min(d, E - 1)].
 constexpr int kBiasNone = 0, kBiasSlope = 1, kBiasTable = 2;
 
-template <int kKind>
+// Lazy-rescale slack of the fp8-P variant, log2 units: with P = 2^(x - m + 8)
+// and x <= m + slack, P stays below 2^8.75 < 448 (the pages' 0.75, under
+// the invariant log2(448) - 8 = 0.807).
+constexpr float kLazySlack = 0.75f;
+
+template <int kKind, bool kP8>
 __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blocks) {
   __shared__ PrefillSmem sm;
@@ -207,12 +214,17 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
           }
           x.x &= mk[0]; x.y &= mk[1]; x.z &= mk[2]; x.w &= mk[3];
         }
-        // tokens 0..7 -> half 0, 8..15 -> half 1, as bf16
         const int dim = off >> 4;
-        sm.v[(pg * 2 + 0) * 128 + dim] = make_uint4(e4m3x2_to_bf16x2<false>(x.x), e4m3x2_to_bf16x2<true>(x.x),
-                                                     e4m3x2_to_bf16x2<false>(x.y), e4m3x2_to_bf16x2<true>(x.y));
-        sm.v[(pg * 2 + 1) * 128 + dim] = make_uint4(e4m3x2_to_bf16x2<false>(x.z), e4m3x2_to_bf16x2<true>(x.z),
-                                                     e4m3x2_to_bf16x2<false>(x.w), e4m3x2_to_bf16x2<true>(x.w));
+        if constexpr (kP8) {
+          // e4m3 as stored: the 16 tokens of one dim of one page
+          sm.v[pg * 128 + dim] = x;
+        } else {
+          // tokens 0..7 -> half 0, 8..15 -> half 1, as bf16
+          sm.v[(pg * 2 + 0) * 128 + dim] = make_uint4(e4m3x2_to_bf16x2<false>(x.x), e4m3x2_to_bf16x2<true>(x.x),
+                                                       e4m3x2_to_bf16x2<false>(x.y), e4m3x2_to_bf16x2<true>(x.y));
+          sm.v[(pg * 2 + 1) * 128 + dim] = make_uint4(e4m3x2_to_bf16x2<false>(x.z), e4m3x2_to_bf16x2<true>(x.z),
+                                                       e4m3x2_to_bf16x2<false>(x.w), e4m3x2_to_bf16x2<true>(x.w));
+        }
       }
     }
   };
@@ -263,6 +275,7 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
       s[1][j] = mfma_16x16x128_e4m3(kop, qop[1], v4f{0.f, 0.f, 0.f, 0.f});
     }
     uint4 pk[2][4];     // P in bf16: pk[cb][kk] holds keys 8kk .. 8kk+7 of the lane group
+    v8i pk8[2];         // fp8-P variant: byte 4j + i of pk8[cb] is key 32*grp + 4j + i
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       const int r = cb * 16 + row;
@@ -301,6 +314,28 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
       bmax = wave_max_xor(bmax, 16);
       bmax = wave_max_xor(bmax, 32);
       const float scale = kBias ? 1.0f : fold;
+      if constexpr (kP8) {
+        // single e4m3 term P = 2^(x - m + 8); the running max is raised (to
+        // the block max) only when a score passes it by more than the slack
+        const float xmax = bmax * scale;
+        const bool raise = xmax > m_run[cb] + kLazySlack;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run[cb] - xmax) : 1.0f;   // 0 from -inf
+        if (raise) m_run[cb] = xmax;
+        const float off8 = 8.0f - (m_run[cb] == -INFINITY ? 0.0f : m_run[cb]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float pv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(s[cb][j][i], scale, off8));
+          pk8[cb][j] = (int)cvt4_e4m3(pv[0], pv[1], pv[2], pv[3]);
+        }
+        if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) o[cb][t] *= alpha;
+          ol[cb] *= alpha;
+        }
+        continue;
+      }
       const float m_new = fmaxf(m_run[cb], bmax * scale);
       const float m_use = m_new == -INFINITY ? 0.0f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_use);
@@ -321,6 +356,30 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
         for (int t = 0; t < 8; ++t) o[cb][t] *= alpha;
         ol[cb] *= alpha;
       }
+    }
+    if constexpr (kP8) {
+      // ---- O^T += V^T P^T on v_mfma_f32_16x16x128_f8f6f4: tile t, dim
+      // 16t + row, keys 32*grp .. +32 = the 16 tokens of block pages 2*grp and
+      // 2*grp + 1; a ones tile accumulates the row sums of the rounded P
+      const v8i ones8 = v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                            0x38383838, 0x38383838, 0x38383838, 0x38383838};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint4 x0 = sm.v[(2 * grp) * 128 + 16 * t + row];
+        const uint4 x1 = sm.v[(2 * grp + 1) * 128 + 16 * t + row];
+        const v8i va = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        o[0][t] = mfma_16x16x128_e4m3(va, pk8[0], o[0][t]);
+        o[1][t] = mfma_16x16x128_e4m3(va, pk8[1], o[1][t]);
+      }
+      ol[0] = mfma_16x16x128_e4m3(ones8, pk8[0], ol[0]);
+      ol[1] = mfma_16x16x128_e4m3(ones8, pk8[1], ol[1]);
+      // operands just in time (two LDS reads, then their two MFMAs)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+      continue;
     }
     // ---- O^T += V^T P^T (bf16 MFMA, 32 keys per step) for both column
     // blocks from one V^T operand read; tile t covers dims 16t .. 16t+15,
@@ -369,15 +428,17 @@ hipError_t launch_prefill_e4m3(const PrefillE4M3Launch &a, hipStream_t s) {
   const int tiles = (a.max_q_len + kTileTok - 1) / kTileTok;
   if (tiles == 0) return hipSuccess;
   const size_t grid = (size_t)8 * ((units + 7) / 8) * tiles;
-  if (a.slopes != nullptr)
-    hipLaunchKernelGGL(prefill_e4m3_kernel<kBiasSlope>, dim3((unsigned)grid), dim3(64 * kPW), 0, s, a, tiles, units,
-                       head_blocks);
-  else if (a.rel != nullptr)
-    hipLaunchKernelGGL(prefill_e4m3_kernel<kBiasTable>, dim3((unsigned)grid), dim3(64 * kPW), 0, s, a, tiles, units,
-                       head_blocks);
-  else
-    hipLaunchKernelGGL(prefill_e4m3_kernel<kBiasNone>, dim3((unsigned)grid), dim3(64 * kPW), 0, s, a, tiles, units,
-                       head_blocks);
+  const dim3 g((unsigned)grid), b(64 * kPW);
+  const int kind = a.slopes != nullptr ? kBiasSlope : (a.rel != nullptr ? kBiasTable : kBiasNone);
+  if (a.fp8_p) {
+    if (kind == kBiasSlope) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasSlope, true>), g, b, 0, s, a, tiles, units, head_blocks);
+    else if (kind == kBiasTable) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasTable, true>), g, b, 0, s, a, tiles, units, head_blocks);
+    else hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasNone, true>), g, b, 0, s, a, tiles, units, head_blocks);
+  } else {
+    if (kind == kBiasSlope) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasSlope, false>), g, b, 0, s, a, tiles, units, head_blocks);
+    else if (kind == kBiasTable) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasTable, false>), g, b, 0, s, a, tiles, units, head_blocks);
+    else hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasNone, false>), g, b, 0, s, a, tiles, units, head_blocks);
+  }
   return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 
 /* A hipStream_t. NULL selects the null stream. */
 typedef struct ihipStream_t *kvq_stream_t;
@@ -121,7 +121,19 @@ typedef struct {
                             bias(h, p, j) = rel_bias[h][min(p - j, rel_extent - 1)]
                             added where the slope bias is. At most one of
                             alibi_slopes and rel_bias may be set. */
+  uint32_t flags;        /* KVQ_FLAG_* bits; other bits must be 0 */
 } kvq_attn_params;
+
+/* kvq_attn_params.flags */
+enum {
+  /* Prefill only (decode ignores it): P = 2^8 p as a single e4m3 term with a
+     lazily raised running max (slack 0.75 in log2 units, under the
+     log2(448) - 8 = 0.807 bound) and PV on fp8 MFMA ([PR54705] evidence
+     "Tier 0"). A speed variant: its error is within the pages' fp8 test
+     tolerance (atol and rtol 0.15, [PR54705] "Test Plan"), not within this
+     library's default attention tolerance, so it is off unless requested. */
+  KVQ_FLAG_PREFILL_FP8_P = 1u
+};
 
 /*
  * kvq_store: quant-on-store ([PR54705] "Purpose", quant-on-store bullet;

@@ -33,7 +33,9 @@ def test_exports_every_declared_symbol(lib):
             "kvq_paged_attn_prefill"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvq_abi_version() == 1
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kvq.h")).read()
+    version = int(re.search(r"#define KVQ_ABI_VERSION (\d+)", hdr).group(1))
+    assert lib.kvq_abi_version() == version == kvq.ABI_VERSION
     for s in (0, -1, -2, -3, -4, -5):
         assert lib.kvq_status_str(s)
 
@@ -47,11 +49,11 @@ def e4m3_desc(**kw):
 
 def params(**kw):
     p = dict(num_q_heads=32, window=0, num_splits=0, rel_extent=0, softmax_scale=0.088,
-             q_scale=1.0, k_scale=1.0, v_scale=1.0, alibi_slopes=None, rel_bias=None)
+             q_scale=1.0, k_scale=1.0, v_scale=1.0, alibi_slopes=None, rel_bias=None, flags=0)
     p.update(kw)
     return kvq.AttnParams(p["num_q_heads"], p["window"], p["num_splits"], p["rel_extent"],
                           p["softmax_scale"], p["q_scale"], p["k_scale"], p["v_scale"],
-                          p["alibi_slopes"], p["rel_bias"])
+                          p["alibi_slopes"], p["rel_bias"], p["flags"])
 
 
 def store(lib, desc, T=4, ks=1.0, vs=1.0, k=FAKE, v=FAKE, stride=512, slot=FAKE):
@@ -106,6 +108,8 @@ def test_decode_validation(lib):
     assert decode(lib, d, params(rel_bias=FAKE + 1, rel_extent=128)) == -1   # misaligned bf16
     assert decode(lib, d, params(rel_bias=FAKE, rel_extent=128, alibi_slopes=FAKE)) == -1
     assert decode(lib, d, params(rel_bias=FAKE, rel_extent=128), B=0) == 0
+    assert decode(lib, d, params(flags=2)) == -1                     # unknown flag bit
+    assert decode(lib, d, params(flags=1), B=0) == 0                 # the prefill flag: ignored here
     for bad in (0.0, -2.0, math.nan, math.inf):
         assert decode(lib, d, params(softmax_scale=bad)) == -3
         assert decode(lib, d, params(q_scale=bad)) == -3

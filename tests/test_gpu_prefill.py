@@ -10,13 +10,13 @@ from parity import DeviceCase, oracle_scales, oracle_cache, seq_tokens, check_at
 pytestmark = pytest.mark.gpu
 
 
-def run_case(c, rows=None, seqs=None):
+def run_case(c, rows=None, seqs=None, **kw):
     dc = DeviceCase(c)
     s = dc.calibrate()
     so = oracle_scales(c)
     assert s == so
     dc.store_all(s)
-    out = dc.prefill(s)
+    out = dc.prefill(s, **kw)
     torch.cuda.synchronize()
     tok = None if seqs is None else seq_tokens(c, seqs)
     kc, vc = oracle_cache(c, so, tokens=tok)
@@ -93,3 +93,55 @@ def test_prefill_poisoned_pool_and_determinism():
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(a.float()))
     assert torch.equal(a, b)
+
+
+def check_fp8_p(out, ref, label):
+    """The single-term e4m3 P variant against the exact oracle: within the
+    pages' fp8 attention test tolerance, atol = rtol = 0.15 (vLLM PR 54705,
+    "Test Plan"), elementwise. Returns the measured errors."""
+    o = out.float().cpu().numpy().astype(np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    err = np.abs(o - r)
+    bad = err > 0.15 + 0.15 * np.abs(r)
+    assert not bad.any(), (label, np.argwhere(bad)[:5])
+    assert np.all(np.isfinite(o))
+    return {"max_abs": float(err.max()), "rel_l2": float(np.linalg.norm(o - r) / max(np.linalg.norm(r), 1e-30))}
+
+
+FP8P_CASES = [
+    # (seq_lens, q_lens, Hq, Hkv, window, bias): bias None / "slopes" / extent
+    ([137, 64, 501], [37, 64, 1], 32, 4, 0, "slopes"),
+    ([137, 64, 501], [37, 64, 1], 32, 4, 0, None),
+    ([300, 1000], [300, 33], 16, 2, 64, "slopes"),
+    ([2600, 777], [129, 777], 8, 1, 0, 1024),
+    ([100, 50, 33], [0, 50, 0], 8, 2, 0, "slopes"),
+]
+
+
+@pytest.mark.parametrize("lens,qlens,hq,hkv,window,bias", FP8P_CASES)
+def test_prefill_fp8_p_variant(lens, qlens, hq, hkv, window, bias):
+    kw = {}
+    if bias == "slopes":
+        kw["slopes"] = geometric_slopes(hq)
+    elif bias is not None:
+        kw["rel_extent"] = bias
+    c = make_attn_case("prefill_p8", 500 + sum(qlens) + hq, lens, qlens, hq, hkv, 128,
+                       v_std=2.0, window=window, **kw)
+    dc, out, ref = run_case(c, fp8_p=True)
+    print(check_fp8_p(out, ref, "fp8 P %s %s w%d %s" % (lens, qlens, window, bias)))
+    s = dc.calibrate()
+    again = dc.prefill(s, fp8_p=True)
+    torch.cuda.synchronize()
+    assert torch.equal(again, out)
+
+
+def test_chunked_prefill_fp8_p_full_size_sampled():
+    c = config_chunked_prefill()
+    rng = np.random.default_rng(1)
+    rows = []
+    for b in (1, 3):
+        r0 = int(c.cu_q_lens[b])
+        picks = np.concatenate([[0, 2047], rng.choice(2048, 30, replace=False)])
+        rows += list(r0 + np.unique(picks))
+    _, out, ref = run_case(c, rows=rows, seqs=[1, 3], fp8_p=True)
+    print(check_fp8_p(out, ref, "chunked_prefill fp8 P"))
