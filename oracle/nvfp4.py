@@ -28,9 +28,22 @@ Decode: latent = e2m1(v) * e4m3(sg) * s2 and RoPE = e4m3(r) * rope_scale;
 attention runs with one KV head, K = [latent ; RoPE] (576 dims), V = latent
 (512 dims), on bf16 Q that is not quantized.
 
+Static outer scale (same page, "Why": with an implicit outer scale of 1.0,
+low-magnitude layers put many group scales in E4M3's subnormal range; the
+commit message: the earlier writer's outer scale was statically 1.0, or a
+per-layer calibrated constant): encode_records(..., static_s2=c) writes the
+same record with s2 = c for every token, for the A/B against the per-token
+scale. Prefill (same page, "Changes" and "Validation": the readers apply the
+per-token scale in decode and in the multitile prefill): query i of a
+sequence with Lq new tokens and L keys sits at position L - Lq + i and attends
+keys j <= its position, with decode's arithmetic.
+
 Pins: tests/test_oracle_nvfp4.py (e2m1 brute force and tie set, a token with
 amax 168 whose scales are exact, power-of-two invariance, s2 read-back,
-no subnormal group scales on the layer-std range).
+no subnormal group scales on the layer-std range; static s2 equal to a
+token's own s2 gives its dynamic record, static 1.0 puts low-magnitude group
+scales into subnormals; every prefill row equals decode over the sequence cut
+at its position).
 """
 from __future__ import annotations
 
@@ -51,21 +64,25 @@ OFF_ROPE = 304
 S2_DIVISOR = 2688.0   # 6 (e2m1 max) * 448 (e4m3 max)
 
 
-def encode_records(x: np.ndarray, rope_scale: float = 1.0) -> np.ndarray:
-    """bf16 tokens (as float32) [T, 576] -> uint8 records [T, 368]."""
+def encode_records(x: np.ndarray, rope_scale: float = 1.0, static_s2=None) -> np.ndarray:
+    """bf16 tokens (as float32) [T, 576] -> uint8 records [T, 368]. static_s2:
+    one outer scale for every token instead of the per-token amax / 2688."""
     x = np.asarray(x, dtype=np.float32)
     T = x.shape[0]
     lat = x[:, :LATENT]
     rope = x[:, LATENT:LATENT + ROPE]
     rec = np.zeros((T, RECORD_BYTES), dtype=np.uint8)
     amax = np.max(np.abs(lat), axis=1) if T else np.zeros(0, np.float32)
-    s2 = (amax / np.float32(S2_DIVISOR)).astype(np.float32)
+    if static_s2 is None:
+        s2 = (amax / np.float32(S2_DIVISOR)).astype(np.float32)
+    else:
+        s2 = np.full(T, np.float32(static_s2), dtype=np.float32)
     d = (np.float32(6.0) * s2).astype(np.float32)
     g = lat.reshape(T, NGROUPS, GROUP)
     ag = np.max(np.abs(g), axis=2)
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = (ag / d[:, None]).astype(np.float32)
-    ratio = np.where(amax[:, None] > 0, ratio, np.float32(0.0))
+    ratio = np.where((amax[:, None] > 0) & (s2[:, None] > 0), ratio, np.float32(0.0))
     ratio = np.minimum(ratio, np.float32(448.0))
     sg = e4m3_encode(ratio)
     dg = (e4m3_decode(sg).astype(np.float32) * s2[:, None]).astype(np.float32)
@@ -109,12 +126,12 @@ def new_pool(num_pages: int, page_size: int = 16, fill: int = 0x7F) -> np.ndarra
 
 
 def store_records(pool: np.ndarray, x: np.ndarray, slot_mapping: np.ndarray,
-                  rope_scale: float = 1.0) -> None:
+                  rope_scale: float = 1.0, static_s2=None) -> None:
     """Encode tokens [T, 576] and write each record at its slot (in place)."""
     page_size = pool.shape[1]
     slot = np.asarray(slot_mapping, dtype=np.int64)
     keep = slot >= 0
-    rec = encode_records(np.asarray(x, dtype=np.float32)[keep], rope_scale)
+    rec = encode_records(np.asarray(x, dtype=np.float32)[keep], rope_scale, static_s2)
     s = slot[keep]
     pool[s // page_size, s % page_size, :] = rec
 
@@ -141,4 +158,38 @@ def mla_decode(q: np.ndarray, pool: np.ndarray, block_table: np.ndarray,
         m = s.max(axis=1, keepdims=True)
         w = np.exp(s - m)
         out[b] = (w @ latent) / w.sum(axis=1, keepdims=True)
+    return out
+
+
+def mla_prefill(q: np.ndarray, cu_q_lens: np.ndarray, pool: np.ndarray, block_table: np.ndarray,
+                seq_lens: np.ndarray, softmax_scale: float, rope_scale: float = 1.0,
+                rows=None) -> np.ndarray:
+    """New queries of sequence b: rows cu_q_lens[b] .. cu_q_lens[b+1]-1 of
+    q [sumQ, Hq, 576] (float32 bf16 values), query i at position L - Lq + i,
+    causal over the sequence's records. ``rows`` restricts the computed rows
+    (global indices); others stay zero. Returns fp64 [sumQ, Hq, 512]."""
+    nrows, Hq, _ = q.shape
+    page_size = pool.shape[1]
+    out = np.zeros((nrows, Hq, LATENT), dtype=np.float64)
+    want = None
+    if rows is not None:
+        want = np.zeros(nrows, dtype=bool)
+        want[np.asarray(rows, dtype=np.int64)] = True
+    for b in range(len(seq_lens)):
+        r0, r1 = int(cu_q_lens[b]), int(cu_q_lens[b + 1])
+        L = int(seq_lens[b])
+        idx = np.arange(r0, r1)
+        if want is not None:
+            idx = idx[want[r0:r1]]
+        if idx.size == 0 or L == 0:
+            continue
+        pos_all = np.arange(L, dtype=np.int64)
+        page = np.asarray(block_table[b], dtype=np.int64)[pos_all // page_size]
+        latent, rope = decode_records(pool[page, pos_all % page_size, :], rope_scale)
+        kfull = np.concatenate([latent, rope], axis=1)
+        qpos = L - (r1 - r0) + (idx - r0)
+        for r, p in zip(idx, qpos):
+            s = (np.asarray(q[r], dtype=np.float64) @ kfull[:p + 1].T) * float(softmax_scale)
+            w = np.exp(s - s.max(axis=1, keepdims=True))
+            out[r] = (w @ latent[:p + 1]) / w.sum(axis=1, keepdims=True)
     return out

@@ -137,3 +137,62 @@ def test_mla_decode_matches_bruteforce():
             want = [sum(w[j] * vals[j][d] for j in range(L)) / tot for d in range(512)]
             assert np.max(np.abs(out[b, h] - np.array(want))) < 1e-12
         start += L
+
+
+def test_static_s2_equal_to_the_token_scale_gives_the_dynamic_record():
+    rng = np.random.default_rng(12)
+    x = token(rng, 0.7, 20)
+    dyn = encode_records(x, 0.5)
+    for i in range(20):
+        assert np.array_equal(encode_records(x[i:i + 1], 0.5, static_s2=record_s2(dyn[i:i + 1])[0]), dyn[i:i + 1])
+
+
+def test_static_outer_scale_reproduces_the_subnormal_failure_mode():
+    """The A/B of the page's "Why": with an outer scale fixed at 1.0 the group
+    scales of low-magnitude latents sink into e4m3's subnormal range and the
+    reconstruction error grows as the magnitude shrinks, up to scales that
+    flush to zero; the per-token scale keeps every group scale normal and the
+    error flat (it is then the e2m1 rounding, about 9.5%)."""
+    rng = np.random.default_rng(13)
+
+    def err(x, rec):
+        lat, _ = decode_records(rec)
+        return np.linalg.norm(lat - x[:, :512]) / np.linalg.norm(x[:, :512])
+
+    sub = lambda r: np.mean((r[:, OFF_GSCALE:OFF_GSCALE + 32] & 0x78) == 0)
+    prev = 0.0
+    for std in (1.0, 0.05, 0.01, 0.002):
+        x = token(rng, std, 512)
+        dyn, sta = encode_records(x), encode_records(x, static_s2=1.0)
+        assert sub(dyn) == 0 and 0.09 < err(x, dyn) < 0.10
+        e = err(x, sta)
+        assert e >= prev - 1e-3
+        prev = e
+        if std == 1.0:
+            assert sub(sta) == 0 and abs(e - err(x, dyn)) < 2e-3
+        if std == 0.01:
+            assert sub(sta) == 1.0 and e > 1.2 * err(x, dyn)
+        if std == 0.002:
+            assert np.mean(sta[:, OFF_GSCALE:OFF_GSCALE + 32] == 0) > 0.5 and e > 0.5
+
+
+def test_mla_prefill_rows_equal_decode_on_the_cut_sequence():
+    """Every prefill row equals decode over its sequence cut at its position:
+    row i of a sequence with Lq new tokens and L keys sits at L - Lq + i."""
+    from oracle.nvfp4 import mla_prefill
+    c = make_mla_case("mp", 14, [40, 17, 70], num_q_heads=4, layer_std=0.6)
+    pool = new_pool(c.num_pages)
+    store_records(pool, c.kv.float().numpy(), c.slot_mapping, 0.75)
+    rng = np.random.default_rng(15)
+    q_lens = np.array([5, 17, 1])
+    cu = np.concatenate([[0], np.cumsum(q_lens)])
+    q = bf16_round(rng.standard_normal((int(cu[-1]), 4, 576)).astype(np.float32))
+    out = mla_prefill(q, cu, pool, c.block_table, c.seq_lens, 0.04, 0.75)
+    for b in range(3):
+        L, lq = int(c.seq_lens[b]), int(q_lens[b])
+        for i in range(lq):
+            r = int(cu[b]) + i
+            want = mla_decode(q[r:r + 1], pool, c.block_table[b:b + 1], np.array([L - lq + i + 1]), 0.04, 0.75)[0]
+            assert np.max(np.abs(out[r] - want)) < 1e-12
+    part = mla_prefill(q, cu, pool, c.block_table, c.seq_lens, 0.04, 0.75, rows=[3, 20])
+    assert np.array_equal(part[[3, 20]], out[[3, 20]]) and not part[0].any()
