@@ -29,6 +29,7 @@ import numpy as np
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 FP8_PEAK_TFLOPS = 5000.0        # dense fp8 MFMA
+FP16_PEAK_TFLOPS = 2500.0       # dense fp16 / bf16 MFMA
 BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -373,16 +374,48 @@ def nvfp4_rows(torch, kvq):
     L = c.max_seq_len
     by = c.batch * (L * 368 + c.num_q_heads * (576 + 512) * 2 + ((L + 15) // 16) * 4 + 4)
     sb = T * (576 * 2 + 368 + 8)
-    del caches
+    del caches, q, out
     torch.cuda.empty_cache()
-    return {"nvfp4_mla_decode": {"batch": c.batch, "context": L, "heads": c.num_q_heads,
+    rows = nvfp4_prefill_rows(torch, kvq)
+    rows.update({"nvfp4_mla_decode": {"batch": c.batch, "context": L, "heads": c.num_q_heads,
                                  "us": round(ms * 1e3, 2), "GB_s": round(by / (ms * 1e-3) / 1e9, 1),
                                  "pct_of_peak": round(100 * by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
                                  "bytes": by},
             "nvfp4_store": {"tokens": T, "us": round(ms_store * 1e3, 2),
                             "tokens_per_s": round(T / (ms_store * 1e-3), 1),
                             "GB_s": round(sb / (ms_store * 1e-3) / 1e9, 1),
-                            "pct_of_peak": round(100 * sb / (ms_store * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}}
+                            "pct_of_peak": round(100 * sb / (ms_store * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}})
+    return rows
+
+
+def nvfp4_prefill_rows(torch, kvq):
+    """NVFP4 chunked prefill: 4 sequences x 16,384 tokens, the last 1,024 new,
+    16 heads. Flops: 2 x (576 + 512) per attended (query row, head, key), the
+    QK^T and PV multiply-adds; the kernel's MFMA runs in fp16."""
+    from workloads import config_nvfp4_mla_prefill
+    log("nvfp4 mla prefill")
+    c = config_nvfp4_mla_prefill()
+    dev = "cuda"
+    cache = kvq.Nvfp4Cache(c.num_pages)
+    kvq.store(cache, c.kv.to(dev), None, torch.from_numpy(c.slot_mapping).to(dev), c.rope_scale)
+    q = c.q.to(dev)
+    cu = torch.from_numpy(c.cu_q_lens).to(dev)
+    bt = torch.from_numpy(c.block_table).to(dev)
+    sl = torch.from_numpy(c.seq_lens).to(dev)
+    out = torch.empty((q.shape[0], c.num_q_heads, 512), dtype=torch.bfloat16, device=dev)
+    ms = timed_mean(torch, lambda: kvq.prefill(cache, q, cu, int(c.q_lens.max()), bt, sl, c.max_seq_len,
+                                               c.softmax_scale, k_scale=c.rope_scale, out=out), reps=5)
+    visits = 0
+    for L, lq in zip(c.seq_lens, c.q_lens):
+        visits += int(np.arange(L - lq + 1, L + 1, dtype=np.int64).sum())
+    fl = 2 * (576 + 512) * c.num_q_heads * visits
+    tf = fl / (ms * 1e-3) / 1e12
+    del cache
+    torch.cuda.empty_cache()
+    return {"nvfp4_mla_prefill": {"batch": c.batch, "new_tokens": int(c.q_lens[0]),
+                                  "context": c.max_seq_len, "us": round(ms * 1e3, 1),
+                                  "TFLOP_s": round(tf, 1), "flops": fl,
+                                  "pct_of_fp16_peak": round(100 * tf / FP16_PEAK_TFLOPS, 2)}}
 
 
 def prefill_flops(seq_lens, q_lens, Hq, D, window=0):

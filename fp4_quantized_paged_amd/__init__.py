@@ -281,15 +281,16 @@ def prefill(cache, q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,
             v_scale: float = 1.0, window: int = 0, slopes: Optional[torch.Tensor] = None,
             out: Optional[torch.Tensor] = None, rel_bias: Optional[torch.Tensor] = None,
             fp8_p: bool = False) -> torch.Tensor:
-    """kvq_paged_attn_prefill. q bf16 [sumQ, Hq, D] -> out bf16 [sumQ, Hq, D].
+    """kvq_paged_attn_prefill. q bf16 [sumQ, Hq, Dqk] -> out bf16 [sumQ, Hq, Dv].
     rel_bias: learned relative-bias table, bf16 [Hq, extent]. fp8_p: the
     single-term e4m3 P speed variant (KVQ_FLAG_PREFILL_FP8_P)."""
     _need_cuda(q, cu_q_lens, block_table, seq_lens, slopes, rel_bias)
     assert q.dtype == torch.bfloat16 and q.is_contiguous()
     total_q, Hq, D = q.shape
     d = cache.desc
+    dv = 512 if d.format == FMT_NVFP4_MLA368 else D
     if out is None:
-        out = torch.empty((total_q, Hq, D), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((total_q, Hq, dv), dtype=torch.bfloat16, device=q.device)
     p = _params(Hq, softmax_scale, q_scale, k_scale, v_scale, window, slopes, 0, rel_bias,
                 FLAG_PREFILL_FP8_P if fp8_p else 0)
     st = lib().kvq_paged_attn_prefill(ctypes.byref(d), _ptr(q), _ptr(cu_q_lens), total_q,

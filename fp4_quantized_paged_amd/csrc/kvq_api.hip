@@ -109,6 +109,7 @@ kvq::DecodePlan plan_decode(const kvq_cache *c, int32_t num_seqs, int32_t max_se
 
 // NVFP4 decode: 64 splits of at most 512 pages
 constexpr int64_t kMlaMaxSeqLen = 64 * 512 * 16;
+constexpr int64_t kMlaPrefillMaxSeqLen = 2048 * 16;   // one split of the MLA kernel
 
 kvq::MlaPlan plan_mla(int32_t num_seqs, int32_t max_seq_len, const kvq_attn_params *p) {
   kvq::MlaPlan pl{};
@@ -324,7 +325,7 @@ int kvq_paged_attn_prefill(const kvq_cache *cache, const void *q, const int32_t 
   (void)workspace_bytes;
   int st = check_cache(cache);
   if (st != KVQ_OK) return st;
-  if (cache->format != KVQ_FMT_E4M3 || cache->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+  if (cache->format == KVQ_FMT_E4M3 && cache->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
   st = check_params(cache, params);
   if (st != KVQ_OK) return st;
   if (num_seqs < 0 || max_seq_len < 0 || total_q < 0 || max_q_len < 0) return KVQ_ERR_INVALID_ARG;
@@ -333,6 +334,24 @@ int kvq_paged_attn_prefill(const kvq_cache *cache, const void *q, const int32_t 
     return KVQ_ERR_INVALID_ARG;
   if (!aligned16(q)) return KVQ_ERR_INVALID_ARG;
   if (block_table_stride * 16 < max_seq_len || max_q_len > max_seq_len) return KVQ_ERR_INVALID_ARG;
+  if (cache->format != KVQ_FMT_E4M3) {
+    if (params->num_q_heads != 16 || max_seq_len > kMlaPrefillMaxSeqLen) return KVQ_ERR_UNSUPPORTED;
+    if (max_q_len == 0) return KVQ_OK;
+    kvq::DecodeMlaLaunch m{};
+    m.q = static_cast<const uint16_t *>(q);
+    m.records = static_cast<const uint8_t *>(cache->k);
+    m.block_table = block_table;
+    m.bt_stride = block_table_stride;
+    m.seq_lens = seq_lens;
+    m.out = static_cast<uint16_t *>(out);
+    m.batch = num_seqs;
+    m.hq = params->num_q_heads;
+    m.scale_log2 = params->softmax_scale * 1.4426950408889634f;
+    m.rope_scale = params->k_scale;
+    m.cu_q_lens = cu_q_lens;
+    m.max_q_len = max_q_len;
+    return hip_status(kvq::launch_prefill_mla(m, max_seq_len, reinterpret_cast<hipStream_t>(stream)));
+  }
   kvq::PrefillE4M3Launch a{};
   a.q = static_cast<const uint16_t *>(q);
   a.cu_q_lens = cu_q_lens;

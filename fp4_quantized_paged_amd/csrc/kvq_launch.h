@@ -104,7 +104,12 @@ struct DecodeMlaLaunch {
   int batch, hq;
   float scale_log2;            // softmax_scale * log2(e)
   float rope_scale;
+  // prefill (extend) mode when cu_q_lens is set: q / out rows
+  // cu_q_lens[b] .. cu_q_lens[b+1]-1, one workgroup per row, one split
+  const int32_t *cu_q_lens;
+  int max_q_len;
 };
+hipError_t launch_prefill_mla(const DecodeMlaLaunch &a, int max_seq_len, hipStream_t s);
 struct MlaPlan {
   int splits;
   int pages_per_split;

@@ -57,7 +57,8 @@ constexpr int kStageRowU4 = (kLat + 64) / 8 + 1;  // bf16 Q staging row, uint4 u
 constexpr float kTau = 8.0f;                      // lazy-max slack, log2 units
 constexpr int kGUnset = -(1 << 20);               // Gs before any nonzero outer scale
 constexpr int kSlabRow = kHalf + 4;               // merge slab row (floats, padded)
-constexpr int kMaxSplitPages = 512;               // pages of one split (the planner's cap)
+constexpr int kBtPerThread = 4;                   // block-table entries staged per thread
+constexpr int kMaxSplitPages = kBtPerThread * kThreads;   // pages of one split (2,048)
 constexpr int kBufs = 4;                          // pages of record bytes in flight per wave
 
 // LDS: two K-row buffers per wave, then the pair exchange. Before the loop
@@ -149,20 +150,38 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   const int half = wave & 1;
   const int row = lane & 15;      // key of the A operand / head of the output
   const int grp = lane >> 4;
-  const int b = blockIdx.x / splits;
-  const int split = blockIdx.x - b * splits;
-
-  const int L = a.seq_lens[b];
+  // Work item. Decode: (sequence b, split), the query is row b. Prefill: the
+  // query row cu_q_lens[b] + i of sequence b with Lq new tokens sits at
+  // position L_b - Lq + i and attends keys 0 .. that position, one split.
+  int b, split, L, qrow;
+  if (a.cu_q_lens != nullptr) {
+    b = blockIdx.x / a.max_q_len;
+    const int i = blockIdx.x - b * a.max_q_len;
+    const int q0 = a.cu_q_lens[b];
+    const int lq = a.cu_q_lens[b + 1] - q0;
+    if (i >= lq) return;   // the whole workgroup: past this sequence's new tokens
+    split = 0;
+    L = max(0, a.seq_lens[b] - lq + i + 1);
+    qrow = q0 + i;
+  } else {
+    b = blockIdx.x / splits;
+    split = blockIdx.x - b * splits;
+    L = a.seq_lens[b];
+    qrow = b;
+  }
   const int npages = (L + 15) >> 4;
   const int p_begin = split * pages_per_split;
   const int p_end = min(npages, p_begin + pages_per_split);
   const int32_t *bt = a.block_table + (size_t)b * a.bt_stride;
-  const int nbt = p_end - p_begin;   // at most kMaxSplitPages = kThreads
+  const int nbt = p_end - p_begin;   // at most kMaxSplitPages
   // Page ids first (clamped indexes keep the loads unconditional): this
   // wave's copy of the split's first 64, and the split's block-table slice
   // (one entry per thread).
   const int btw = bt[p_begin + max(0, min(lane, nbt - 1))];
-  const int btt = bt[p_begin + max(0, min((int)threadIdx.x, nbt - 1))];
+  int btt[kBtPerThread];
+#pragma unroll
+  for (int j = 0; j < kBtPerThread; ++j)
+    btt[j] = bt[p_begin + max(0, min((int)threadIdx.x + j * kThreads, nbt - 1))];
   __builtin_amdgcn_sched_barrier(0);
 
   // coalesced page loads: nibble load i, lane l -> key 8i + l/8, bytes
@@ -174,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   // Every page slot issues the same five loads, so the wait for one buffer
   // never covers the later buffers' loads in flight. Without a page to fetch
   // they read this sequence's Q block instead (18 KB, read anyway, unused).
-  const uint8_t *dummy = (const uint8_t *)(a.q + (size_t)b * a.hq * (kLat + 64));
+  const uint8_t *dummy = (const uint8_t *)(a.q + (size_t)qrow * a.hq * (kLat + 64));
   auto fetch_from = [&](const uint8_t *page, PageRaw &r) {
     r.nib[0] = __builtin_nontemporal_load((const v4u *)(page + off_nib));
     r.nib[1] = __builtin_nontemporal_load((const v4u *)(page + off_nib + 8 * kRec));
@@ -204,12 +223,14 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   {
     // Q is requested behind the first pages, so both arrive in one round trip
     constexpr int kQU4 = kHeads * (kLat + 64) / 8;
-    const uint4 *qsrc = (const uint4 *)(a.q + (size_t)b * a.hq * (kLat + 64));
+    const uint4 *qsrc = (const uint4 *)(a.q + (size_t)qrow * a.hq * (kLat + 64));
     uint4 qv[(kQU4 + kThreads - 1) / kThreads];
 #pragma unroll
     for (int j = 0; j < (kQU4 + kThreads - 1) / kThreads; ++j)
       qv[j] = qsrc[min((int)threadIdx.x + j * kThreads, kQU4 - 1)];
-    if ((int)threadIdx.x < nbt) s_bt[threadIdx.x] = btt;
+#pragma unroll
+    for (int j = 0; j < kBtPerThread; ++j)
+      if ((int)threadIdx.x + j * kThreads < nbt) s_bt[threadIdx.x + j * kThreads] = btt[j];
     uint4 *qs = (uint4 *)smem;
     // unconditional stores: entries past Q (rows 16 .. 21) land in K-row
     // buffer space that is cleared below
@@ -500,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
       uint2 w;
       w.x = f32_to_bf16_bits(acc[0] * sc) | (f32_to_bf16_bits(acc[1] * sc) << 16);
       w.y = f32_to_bf16_bits(acc[2] * sc) | (f32_to_bf16_bits(acc[3] * sc) << 16);
-      *(uint2 *)(a.out + ((size_t)b * a.hq + hd) * kLat + d) = w;
+      *(uint2 *)(a.out + ((size_t)qrow * a.hq + hd) * kLat + d) = w;
     } else {
       const size_t pi = ((size_t)b * a.hq + hd) * splits + split;
       *(v4f *)(a.part_o + pi * kLat + d) = acc;
@@ -555,6 +576,15 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const floa
 }
 
 }  // namespace
+
+hipError_t launch_prefill_mla(const DecodeMlaLaunch &a, int max_seq_len, hipStream_t s) {
+  if (a.hq != kHeads || a.cu_q_lens == nullptr || a.max_q_len <= 0) return hipErrorInvalidValue;
+  const int pages = (max_seq_len + 15) / 16;
+  if (pages > kMaxSplitPages) return hipErrorNotSupported;
+  hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)((size_t)a.batch * a.max_q_len)), dim3(kThreads), 0, s, a, 1,
+                     pages > 0 ? pages : 1);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_mla(const DecodeMlaLaunch &a, const MlaPlan &p, hipStream_t s) {
   if (a.hq != kHeads) return hipErrorNotSupported;

@@ -251,7 +251,9 @@ int kvq_paged_attn_decode(const kvq_cache *cache, const void *q,
 
 /*
  * kvq_paged_attn_prefill: chunked prefill over the e4m3 cache ([PR54705]
- * "Purpose"; evidence "Tier 1" chunked-prefill case).
+ * "Purpose"; evidence "Tier 1" chunked-prefill case), or over NVFP4 records
+ * ([PR189] "Changes" and "Validation": the readers apply the per-token outer
+ * scale in decode and in prefill).
  *
  * The new queries of sequence b are rows cu_q_lens[b] .. cu_q_lens[b+1]-1 of
  * q bf16 [total_q][num_q_heads][head_dim] (contiguous, 16-byte aligned); query
@@ -260,8 +262,12 @@ int kvq_paged_attn_decode(const kvq_cache *cache, const void *q,
  * (and > position - window when window > 0). Scores, bias and output as in
  * decode. cu_q_lens: device int32 [num_seqs + 1]; max_q_len: host upper
  * bound of the per-sequence query counts. out: bf16 [total_q][num_q_heads]
- * [head_dim]. Only KVQ_FMT_E4M3 is supported. No workspace is needed
- * (workspace may be NULL, workspace_bytes 0).
+ * [head_dim_v]. KVQ_FMT_E4M3 needs head_dim 128. KVQ_FMT_NVFP4_MLA368: q is
+ * bf16 [total_q][16][576] (not quantized), out bf16 [total_q][16][512], the
+ * arithmetic of the NVFP4 decode; num_q_heads must be 16, max_seq_len at
+ * most 32,768, window 0 and both biases NULL (KVQ_ERR_UNSUPPORTED
+ * otherwise). No workspace is needed (workspace may be NULL,
+ * workspace_bytes 0).
  */
 int kvq_paged_attn_prefill(const kvq_cache *cache, const void *q, const int32_t *cu_q_lens,
                            int64_t total_q, int32_t max_q_len, const int32_t *block_table,

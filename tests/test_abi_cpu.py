@@ -150,9 +150,16 @@ def test_prefill_validation(lib):
     assert f(ctypes.byref(d), FAKE, FAKE, 0, 0, FAKE, 64, FAKE, 2, 100, ctypes.byref(p), FAKE, None, 0, None) == 0
     assert f(ctypes.byref(d), FAKE, FAKE, 10, 200, FAKE, 64, FAKE, 2, 100, ctypes.byref(p), FAKE, None, 0,
              None) == -1                                        # max_q_len > max_seq_len
+    # NVFP4 prefill: validation only (no call below reaches a launch)
     nv = kvq.CacheDesc(2, 16, 1, 576, 64, FAKE, None)
-    assert f(ctypes.byref(nv), FAKE, FAKE, 10, 5, FAKE, 64, FAKE, 2, 100, ctypes.byref(params(num_q_heads=16)),
-             FAKE, None, 0, None) == -2
+    assert f(ctypes.byref(nv), FAKE, FAKE, 10, 5, FAKE, 64, FAKE, 2, 100, ctypes.byref(params(num_q_heads=8)),
+             FAKE, None, 0, None) == -2                           # 16 heads only
+    assert f(ctypes.byref(nv), FAKE, FAKE, 10, 5, FAKE, 4096, FAKE, 2, 40000,
+             ctypes.byref(params(num_q_heads=16)), FAKE, None, 0, None) == -2   # past 32,768 keys
+    assert f(ctypes.byref(nv), FAKE, FAKE, 10, 5, FAKE, 64, FAKE, 2, 100,
+             ctypes.byref(params(num_q_heads=16, window=64)), FAKE, None, 0, None) == -2
+    assert f(ctypes.byref(nv), FAKE, FAKE, 0, 0, FAKE, 64, FAKE, 2, 100, ctypes.byref(params(num_q_heads=16)),
+             FAKE, None, 0, None) == 0                            # no queries: no launch
 
 
 def test_struct_layouts_match_header(tmp_path):

@@ -117,3 +117,82 @@ def test_mla_decode_full_size_sampled(layer):
     c = config_nvfp4_mla(layer=layer)
     out, ref = run_mla(c, seqs=[0, 7, 19, 31])
     print(check_attention(out, ref, "nvfp4 mla layer %d" % layer))
+
+
+def run_mla_prefill(c, q_lens, seed, rows=None):
+    """NVFP4 prefill: the case's records hold every token; q_lens new query
+    rows per sequence (the last tokens) are drawn here."""
+    from oracle.nvfp4 import mla_prefill
+    rng = np.random.default_rng(seed)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    q = bf16(rng.standard_normal((int(cu[-1]), 16, 576)).astype(np.float32))
+    cache = kvq.Nvfp4Cache(c.num_pages)
+    kvq.store(cache, c.kv.cuda(), None, torch.from_numpy(c.slot_mapping).cuda(), c.rope_scale)
+    out = kvq.prefill(cache, q.cuda(), torch.from_numpy(cu).cuda(), int(q_lens.max()),
+                      torch.from_numpy(c.block_table).cuda(), torch.from_numpy(c.seq_lens).cuda(),
+                      c.max_seq_len, c.softmax_scale, k_scale=c.rope_scale)
+    torch.cuda.synchronize()
+    pool = new_pool(c.num_pages)
+    store_records(pool, c.kv.float().numpy(), c.slot_mapping, c.rope_scale)
+    ref = mla_prefill(q.float().numpy(), cu, pool, c.block_table, c.seq_lens, c.softmax_scale,
+                      c.rope_scale, rows=rows)
+    if rows is not None:
+        return out[torch.tensor(rows)], ref[rows]
+    return out, ref
+
+
+@pytest.mark.parametrize("std", [0.05, 1.0, 4.0])
+def test_mla_prefill_shapes(std):
+    """Ragged new-token counts, a whole-sequence prefill, a sequence without
+    new tokens, partial last pages."""
+    c = make_mla_case("mla_pf", 70 + int(std * 10), [40, 17, 300, 9, 1000], layer_std=std, rope_scale=0.8)
+    out, ref = run_mla_prefill(c, [5, 17, 1, 0, 129], 71)
+    print(check_attention(out, ref, "mla prefill std %g" % std))
+
+
+def test_mla_prefill_long_sampled():
+    """Two sequences of 8,192 keys with 256 and 64 new tokens; 40 sampled rows."""
+    c = make_mla_case("mla_pf_long", 72, [8192, 8192], layer_std=1.0)
+    rng = np.random.default_rng(3)
+    rows = sorted(set([0, 255, 256, 319] + list(rng.choice(320, 36, replace=False))))
+    out, ref = run_mla_prefill(c, [256, 64], 73, rows=rows)
+    print(check_attention(out, ref, "mla prefill 2 x 8192"))
+
+
+def test_mla_prefill_one_token_equals_decode():
+    """One new token per sequence is decode: the prefill rows equal the
+    single-split decode output bit for bit (same kernel, same key order)."""
+    c = make_mla_case("mla_pf1", 74, [1, 16, 17, 300, 2049], layer_std=1.0)
+    cache = kvq.Nvfp4Cache(c.num_pages)
+    kvq.store(cache, c.kv.cuda(), None, torch.from_numpy(c.slot_mapping).cuda(), c.rope_scale)
+    bt = torch.from_numpy(c.block_table).cuda()
+    sl = torch.from_numpy(c.seq_lens).cuda()
+    q = c.q.cuda()
+    dec = kvq.decode(cache, q, bt, sl, c.max_seq_len, c.softmax_scale, num_splits=1)
+    cu = torch.arange(c.batch + 1, dtype=torch.int32, device="cuda")
+    pf = kvq.prefill(cache, q, cu, 1, bt, sl, c.max_seq_len, c.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(dec, pf)
+
+
+def test_mla_prefill_full_size_sampled():
+    """The prefill workload the bench times (4 x 16,384 tokens, last 1,024
+    new), in the same launch; 24 sampled rows against the oracle."""
+    from oracle.nvfp4 import mla_prefill
+    from workloads import config_nvfp4_mla_prefill
+    c = config_nvfp4_mla_prefill()
+    cache = kvq.Nvfp4Cache(c.num_pages)
+    kvq.store(cache, c.kv.cuda(), None, torch.from_numpy(c.slot_mapping).cuda(), c.rope_scale)
+    cu = c.cu_q_lens
+    out = kvq.prefill(cache, c.q.cuda(), torch.from_numpy(cu).cuda(), int(c.q_lens.max()),
+                      torch.from_numpy(c.block_table).cuda(), torch.from_numpy(c.seq_lens).cuda(),
+                      c.max_seq_len, c.softmax_scale, k_scale=c.rope_scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    rows = sorted(set([0, 1023, 1024, int(cu[-1]) - 1] + list(rng.choice(int(cu[-1]), 20, replace=False))))
+    pool = new_pool(c.num_pages)
+    store_records(pool, c.kv.float().numpy(), c.slot_mapping, c.rope_scale)
+    ref = mla_prefill(c.q.float().numpy(), cu, pool, c.block_table, c.seq_lens, c.softmax_scale,
+                      c.rope_scale, rows=rows)
+    print(check_attention(out[torch.tensor(rows)], ref[rows], "nvfp4 mla prefill full size"))

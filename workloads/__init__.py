@@ -27,6 +27,7 @@ from .gen import (  # noqa: F401
     config_long_context,
     config_chunked_prefill,
     config_nvfp4_mla,
+    config_nvfp4_mla_prefill,
     geometric_slopes,
     CONFIGS,
 )

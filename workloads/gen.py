@@ -264,10 +264,15 @@ class MlaCase:
     layer_std: float
     rope_scale: float = 1.0
     softmax_scale: float = 1.0
+    q_lens: Optional[np.ndarray] = None   # prefill: new tokens per sequence; q is [sum, Hq, D]
 
     @property
     def batch(self) -> int:
         return int(len(self.seq_lens))
+
+    @property
+    def cu_q_lens(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.q_lens)]).astype(np.int32)
 
     @property
     def max_seq_len(self) -> int:
@@ -308,10 +313,22 @@ def config_nvfp4_mla(layer: int = 0, seed: int = 4, batch: int = 32,
                          16, layer_std=std)
 
 
+def config_nvfp4_mla_prefill(seed: int = 5, batch: int = 4, context: int = 16384,
+                             new: int = 1024, layer_std: float = 1.0) -> MlaCase:
+    """Chunked prefill over the NVFP4 latent cache: 4 sequences whose last
+    1,024 of 16,384 tokens are new, 16 query heads, N(0,1) queries."""
+    c = make_mla_case("nvfp4_mla_prefill", seed, [context] * batch, 16, layer_std=layer_std)
+    rng = np.random.default_rng(seed + 1000)
+    c.q_lens = np.full(batch, new, dtype=np.int32)
+    c.q = bf16(_normal(rng, (batch * new, c.num_q_heads, c.latent_dim + c.rope_dim), 1.0))
+    return c
+
+
 CONFIGS = {
     "tiny_decode": config_tiny_decode,
     "batched_decode": config_batched_decode,
     "long_context": config_long_context,
     "chunked_prefill": config_chunked_prefill,
     "nvfp4_mla": config_nvfp4_mla,
+    "nvfp4_mla_prefill": config_nvfp4_mla_prefill,
 }
