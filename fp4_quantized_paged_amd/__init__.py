@@ -49,7 +49,7 @@ FLAG_PREFILL_FP8_P = 1
 
 
 _lib = None
-ABI_VERSION = 2   # KVQ_ABI_VERSION of include/kvq.h
+ABI_VERSION = 3   # KVQ_ABI_VERSION of include/kvq.h
 
 _SIGNATURES = {
     "kvq_abi_version": (ctypes.c_int, []),
@@ -57,6 +57,9 @@ _SIGNATURES = {
     "kvq_store": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p, ctypes.c_int64,
                                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                  ctypes.c_float, ctypes.c_float, ctypes.c_void_p]),
+    "kvq_store_nvfp4_static": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p, ctypes.c_int64,
+                                              ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                                              ctypes.c_float, ctypes.c_void_p]),
     "kvq_calibrate_amax": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p]),
@@ -88,13 +91,15 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError("libkvq.so not found at %s: build it with "
                                "`python -m fp4_quantized_paged_amd.build`" % LIB_PATH)
         handle = ctypes.CDLL(LIB_PATH)
+        handle.kvq_abi_version.restype = ctypes.c_int
+        handle.kvq_abi_version.argtypes = []
+        if handle.kvq_abi_version() != ABI_VERSION:
+            raise RuntimeError("%s has ABI version %d, this binding expects %d: rebuild it"
+                               % (LIB_PATH, handle.kvq_abi_version(), ABI_VERSION))
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args
-        if handle.kvq_abi_version() != ABI_VERSION:
-            raise RuntimeError("%s has ABI version %d, this binding expects %d: rebuild it"
-                               % (LIB_PATH, handle.kvq_abi_version(), ABI_VERSION))
         _lib = handle
     return _lib
 
@@ -168,6 +173,17 @@ def store(cache, k: torch.Tensor, v: Optional[torch.Tensor], slot_mapping: torch
                          v.stride(0) if v is not None else 0, _ptr(slot_mapping), T,
                          float(k_scale), float(v_scale), _stream())
     _check(st, "kvq_store")
+
+
+def store_nvfp4_static(cache, x: torch.Tensor, slot_mapping: torch.Tensor, rope_scale: float,
+                       outer_scale: float) -> None:
+    """kvq_store_nvfp4_static: NVFP4 records with one static outer scale for
+    every token. x bf16 [T, 576], slot_mapping int64 [T]."""
+    _need_cuda(x, slot_mapping)
+    assert slot_mapping.dtype == torch.int64 and x.dtype == torch.bfloat16
+    st = lib().kvq_store_nvfp4_static(ctypes.byref(cache.desc), _ptr(x), x.stride(0), _ptr(slot_mapping),
+                                      x.shape[0], float(rope_scale), float(outer_scale), _stream())
+    _check(st, "kvq_store_nvfp4_static")
 
 
 def calibrate_amax(x: torch.Tensor, slot_mapping: Optional[torch.Tensor] = None,

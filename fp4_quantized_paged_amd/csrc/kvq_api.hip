@@ -196,6 +196,29 @@ int kvq_store(const kvq_cache *cache, const void *k, int64_t k_token_stride, con
   a.num_tokens = num_tokens;
   a.records = static_cast<uint8_t *>(cache->k);
   a.rope_inv = 1.0f / k_scale;
+  a.static_s2 = 0.0f;
+  return hip_status(kvq::launch_store_nvfp4(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int kvq_store_nvfp4_static(const kvq_cache *cache, const void *x, int64_t token_stride,
+                           const int64_t *slot_mapping, int64_t num_tokens, float rope_scale,
+                           float outer_scale, kvq_stream_t stream) {
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (cache->format != KVQ_FMT_NVFP4_MLA368) return KVQ_ERR_UNSUPPORTED;
+  if (num_tokens < 0) return KVQ_ERR_INVALID_ARG;
+  if (!good_scale(rope_scale) || !good_scale(outer_scale)) return KVQ_ERR_BAD_SCALE;
+  if (num_tokens == 0) return KVQ_OK;
+  if (x == nullptr || slot_mapping == nullptr || !aligned16(x)) return KVQ_ERR_INVALID_ARG;
+  if (token_stride < 576 || token_stride % 8) return KVQ_ERR_INVALID_ARG;
+  kvq::StoreNvfp4Launch a{};
+  a.x = static_cast<const uint16_t *>(x);
+  a.stride = token_stride;
+  a.slot = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.records = static_cast<uint8_t *>(cache->k);
+  a.rope_inv = 1.0f / rope_scale;
+  a.static_s2 = outer_scale;
   return hip_status(kvq::launch_store_nvfp4(a, reinterpret_cast<hipStream_t>(stream)));
 }
 

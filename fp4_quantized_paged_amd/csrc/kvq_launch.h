@@ -25,6 +25,7 @@ struct StoreNvfp4Launch {
   int64_t num_tokens;
   uint8_t *records;            // [pages][16][368]
   float rope_inv;              // fp32(1/rope_scale)
+  float static_s2;             // 0: per-token s2 = amax / 2688; > 0: this outer scale for every token
 };
 hipError_t launch_store_nvfp4(const StoreNvfp4Launch &a, hipStream_t s);
 

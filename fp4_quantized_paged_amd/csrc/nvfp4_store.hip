@@ -12,6 +12,10 @@
 //   dg = fp32(e4m3(sg) * s2); codes = e2m1_RNE(clip(x * fp32(1 / dg), -6, 6)),
 //   or +0 codes when dg == 0 (also for an all-zero token, where s2 = 0)
 //   RoPE: the e4m3 store quantizer with the rope scale
+// Static mode (the writer the same commit message describes before the
+// per-token scale: one outer scale per layer, 1.0 unless calibrated): s2 is
+// that launch constant for every token, with the same formulas; a group whose
+// ratio ag / (6 s2) falls below 2^-6 gets a subnormal or zero scale code.
 // Record: [0,256) values, element 2i in the low nibble of byte i; [256,288)
 // group-scale codes; [288,292) zero; [292,296) s2 (little endian);
 // [296,304) zero; [304,368) RoPE codes.
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void store_nvfp4_kernel(StoreNvfp4Launch 
   const float amax = __uint_as_float(am_bits << 16);
 
   // ---- two-level scales
-  const float s2 = amax / 2688.0f;
+  const float s2 = a.static_s2 > 0.0f ? a.static_s2 : amax / 2688.0f;
   const float d = 6.0f * s2;
   float ratio = amax > 0.0f ? ag / d : 0.0f;
   ratio = fminf(ratio, kE4M3Max);

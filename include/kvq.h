@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 2
+#define KVQ_ABI_VERSION 3
 
 /* A hipStream_t. NULL selects the null stream. */
 typedef struct ihipStream_t *kvq_stream_t;
@@ -156,6 +156,26 @@ enum {
 int kvq_store(const kvq_cache *cache, const void *k, int64_t k_token_stride,
               const void *v, int64_t v_token_stride, const int64_t *slot_mapping,
               int64_t num_tokens, float k_scale, float v_scale, kvq_stream_t stream);
+
+/*
+ * kvq_store_nvfp4_static: the NVFP4 record store with one static outer scale
+ * for every token instead of the per-token one ([PR189] commit message: the
+ * writer's outer scale was statically 1.0, or calibrated per layer by a
+ * separate static mode; "Why": with it, low-magnitude layers put many group
+ * scales into e4m3's subnormal range). It exists for the A/B against the
+ * per-token scale.
+ *
+ * cache must be KVQ_FMT_NVFP4_MLA368 (else KVQ_ERR_UNSUPPORTED). x, token_stride,
+ * slot_mapping, num_tokens and rope_scale as for kvq_store. outer_scale
+ * (finite, > 0, else KVQ_ERR_BAD_SCALE) replaces amax(latent)/2688 as s2 in
+ * every formula of kvq_store and is written to bytes [292, 296), so the
+ * readers of this library decode static and per-token records alike. The
+ * pages' static records carry no scale in the record and take it at launch;
+ * the arithmetic is the same.
+ */
+int kvq_store_nvfp4_static(const kvq_cache *cache, const void *x, int64_t token_stride,
+                           const int64_t *slot_mapping, int64_t num_tokens, float rope_scale,
+                           float outer_scale, kvq_stream_t stream);
 
 /*
  * kvq_calibrate_amax: running amax and scale = amax / 448 ([KVcal] scale

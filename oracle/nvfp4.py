@@ -36,14 +36,16 @@ same record with s2 = c for every token, for the A/B against the per-token
 scale. Prefill (same page, "Changes" and "Validation": the readers apply the
 per-token scale in decode and in the multitile prefill): query i of a
 sequence with Lq new tokens and L keys sits at position L - Lq + i and attends
-keys j <= its position, with decode's arithmetic.
+keys j <= its position, with decode's arithmetic. mla_exact is attention
+over the unquantized tokens, the reference both records are judged against.
 
 Pins: tests/test_oracle_nvfp4.py (e2m1 brute force and tie set, a token with
 amax 168 whose scales are exact, power-of-two invariance, s2 read-back,
 no subnormal group scales on the layer-std range; static s2 equal to a
 token's own s2 gives its dynamic record, static 1.0 puts low-magnitude group
 scales into subnormals; every prefill row equals decode over the sequence cut
-at its position).
+at its position; on tokens the record holds exactly, decode over the records
+equals mla_exact).
 """
 from __future__ import annotations
 
@@ -192,4 +194,24 @@ def mla_prefill(q: np.ndarray, cu_q_lens: np.ndarray, pool: np.ndarray, block_ta
             s = (np.asarray(q[r], dtype=np.float64) @ kfull[:p + 1].T) * float(softmax_scale)
             w = np.exp(s - s.max(axis=1, keepdims=True))
             out[r] = (w @ latent[:p + 1]) / w.sum(axis=1, keepdims=True)
+    return out
+
+
+def mla_exact(q: np.ndarray, kv: np.ndarray, seq_lens: np.ndarray, softmax_scale: float) -> np.ndarray:
+    """Attention over the unquantized tokens (the reference of the static /
+    per-token outer-scale A/B of local-inference-lab/vllm PR 189, "Why"): kv
+    [T, 576] float32 tokens of all sequences back to back, K = the 576 dims,
+    V = the 512 latent dims, one query per sequence. Returns fp64 [B, Hq, 512]."""
+    B, Hq, _ = q.shape
+    out = np.zeros((B, Hq, LATENT), dtype=np.float64)
+    start = 0
+    for b in range(B):
+        L = int(seq_lens[b])
+        k = np.asarray(kv[start:start + L], dtype=np.float64)
+        start += L
+        if L == 0:
+            continue
+        s = (np.asarray(q[b], dtype=np.float64) @ k.T) * float(softmax_scale)
+        w = np.exp(s - s.max(axis=1, keepdims=True))
+        out[b] = (w @ k[:, :LATENT]) / w.sum(axis=1, keepdims=True)
     return out

@@ -84,6 +84,24 @@ def test_store_validation(lib):
     assert lib.kvq_store(ctypes.byref(bad_nv), FAKE, 576, None, 0, FAKE, 4, 1.0, 1.0, None) == -2
 
 
+def test_store_nvfp4_static_validation(lib):
+    f = lib.kvq_store_nvfp4_static
+    nv = kvq.CacheDesc(2, 16, 1, 576, 64, FAKE, None)
+    assert f(None, FAKE, 576, FAKE, 4, 1.0, 1.0, None) == -1
+    assert f(ctypes.byref(e4m3_desc()), FAKE, 576, FAKE, 4, 1.0, 1.0, None) == -2   # e4m3 pools: no
+    assert f(ctypes.byref(kvq.CacheDesc(2, 16, 1, 512, 64, FAKE, None)), FAKE, 576, FAKE, 4, 1.0, 1.0, None) == -2
+    for bad in (0.0, -1.0, math.nan, math.inf):
+        assert f(ctypes.byref(nv), FAKE, 576, FAKE, 4, bad, 1.0, None) == -3      # RoPE scale
+        assert f(ctypes.byref(nv), FAKE, 576, FAKE, 4, 1.0, bad, None) == -3      # outer scale
+    assert f(ctypes.byref(nv), FAKE, 576, FAKE, -1, 1.0, 1.0, None) == -1
+    assert f(ctypes.byref(nv), FAKE, 576, FAKE, 0, 1.0, 1.0, None) == 0          # no launch
+    assert f(ctypes.byref(nv), None, 576, FAKE, 4, 1.0, 1.0, None) == -1
+    assert f(ctypes.byref(nv), FAKE, 576, None, 4, 1.0, 1.0, None) == -1
+    assert f(ctypes.byref(nv), FAKE + 8, 576, FAKE, 4, 1.0, 1.0, None) == -1      # misaligned input
+    assert f(ctypes.byref(nv), FAKE, 570, FAKE, 4, 1.0, 1.0, None) == -1          # stride below a token
+    assert f(ctypes.byref(nv), FAKE, 580, FAKE, 4, 1.0, 1.0, None) == -1          # stride % 8
+
+
 def test_calibrate_validation(lib):
     f = lib.kvq_calibrate_amax
     assert f(FAKE, 10, 512, 512, None, None, None, None) == -1     # no amax buffer

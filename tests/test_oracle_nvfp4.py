@@ -196,3 +196,30 @@ def test_mla_prefill_rows_equal_decode_on_the_cut_sequence():
             assert np.max(np.abs(out[r] - want)) < 1e-12
     part = mla_prefill(q, cu, pool, c.block_table, c.seq_lens, 0.04, 0.75, rows=[3, 20])
     assert np.array_equal(part[[3, 20]], out[[3, 20]]) and not part[0].any()
+
+
+def test_decode_over_lossless_records_equals_exact_attention():
+    """Tokens the record represents exactly (every group holds +-168, the rest
+    of the e2m1 grid times 28, s2 = 2^-4, RoPE small integers): decode over
+    the records and attention over the raw tokens agree to rounding."""
+    from oracle.nvfp4 import mla_exact
+    rng = np.random.default_rng(16)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32) * 28.0
+    seq_lens = np.array([19, 40])
+    T = int(seq_lens.sum())
+    lat = grid[rng.integers(0, 8, (T, 32, 16))] * rng.choice([-1.0, 1.0], (T, 32, 16)).astype(np.float32)
+    lat[:, :, 0] = 168.0 * rng.choice([-1.0, 1.0], (T, 32)).astype(np.float32)
+    x = np.concatenate([lat.reshape(T, 512), rng.integers(-8, 9, (T, 64)).astype(np.float32)], axis=1)
+    rec = encode_records(x)
+    assert np.all(record_s2(rec) == 1.0 / 16)
+    # sequence b, position p sits at page bt[b, p // 16], row p % 16
+    pages = rng.permutation(8)
+    bt = np.array([[pages[0], pages[1], 0, 0], [pages[2], pages[3], pages[4], 0]], np.int32)
+    slot = np.concatenate([bt[0][np.arange(19) // 16] * 16 + np.arange(19) % 16,
+                           bt[1][np.arange(40) // 16] * 16 + np.arange(40) % 16])
+    pool = new_pool(8)
+    store_records(pool, x, slot)
+    q = bf16_round(rng.standard_normal((2, 3, 576)).astype(np.float32) * 0.01)
+    got = mla_decode(q, pool, bt, seq_lens, 0.04)
+    want = mla_exact(q, x, seq_lens, 0.04)
+    assert np.max(np.abs(got - want)) < 1e-9 * np.max(np.abs(want))
