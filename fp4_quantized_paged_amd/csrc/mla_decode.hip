@@ -38,6 +38,11 @@
 //    two) only when m or Gs moves;
 //  * pairs merge through LDS; with one split the workgroup writes bf16, else
 //    (O, m, l, m + Gs) partials go to the workspace for the split combine.
+//
+// Prefill (the same page: the readers apply the per-token scale in decode and
+// in the multitile prefill): one workgroup per new query row, one split over
+// the row's causal prefix; new row i of a sequence with Lq new tokens and L
+// keys attends keys 0 .. L - Lq + i with exactly decode's arithmetic.
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
