@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true", help="no CPU oracle baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a 1 GiB device copy (HBM counter calibration)")
-    ap.add_argument("--only", choices=["prefill", "long_context", "nvfp4"], default=None,
+    ap.add_argument("--only", choices=["prefill", "long_context", "nvfp4", "nvfp4_prefill"], default=None,
                     help="run only this row (for profiling); prints its JSON")
     return ap.parse_args()
 
@@ -174,7 +174,8 @@ def main():
     kvq.lib()   # fail loudly when the HIP library is missing
     torch.cuda.set_device(0)
     if args.only is not None:
-        fn = {"prefill": prefill_rows, "long_context": long_context_rows, "nvfp4": nvfp4_rows}[args.only]
+        fn = {"prefill": prefill_rows, "long_context": long_context_rows, "nvfp4": nvfp4_rows,
+              "nvfp4_prefill": nvfp4_prefill_rows}[args.only]
         print(json.dumps(fn(torch, kvq)), flush=True)
         return
     dev = "cuda"
@@ -325,6 +326,15 @@ def extras(torch, kvq, c, k, v, q, slot, scales):
     kn, vn, sn = k[idx].contiguous(), v[idx].contiguous(), slot[idx].contiguous()
     ms = timed_mean(torch, lambda: kvq.store(cache, kn, vn, sn, scales["k"], scales["v"]), reps=20)
     rows["store_append"] = {"tokens": int(kn.shape[0]), "us": round(ms * 1e3, 2)}
+    # the store sizes of the write-path benchmark on the vLLM PR 54705 page
+    # ("Tier 1"): 33, 2,048 and 16,384 tokens, the workload's first tokens
+    sweep = {}
+    for n in (33, 2048, 16384):
+        kn_, vn_, sn_ = k[:n].contiguous(), v[:n].contiguous(), slot[:n].contiguous()
+        ms = timed_mean(torch, lambda: kvq.store(cache, kn_, vn_, sn_, scales["k"], scales["v"]), reps=20)
+        sweep[str(n)] = {"us": round(ms * 1e3, 2), "tokens_per_s": round(n / (ms * 1e-3), 1),
+                         "GB_s": round(store_bytes(n, Hkv, D) / (ms * 1e-3) / 1e9, 1)}
+    rows["store_sweep"] = sweep
     # calibration over K and V
     amax = torch.zeros(1, device=k.device)
     ms = timed_mean(torch, lambda: (kvq.calibrate_amax(k, amax=amax), kvq.calibrate_amax(v, amax=amax)))

@@ -31,6 +31,13 @@
 //    each wave fills a small LDS table of them (from the slope or from the
 //    learned table) and looks the scores' bias up; with the learned table, a
 //    block entirely beyond its extent adds the last entry instead;
+//  * blocks run from the diagonal outward (nearest keys first), so a row
+//    under a distance-decaying bias meets its largest scores first; the
+//    running max is lazy (raised only when a score passes it by more than 8,
+//    log2 units; bf16 P <= 2^8 keeps its relative precision), so O is rarely
+//    rescaled; and a wave whose every P in a block would be exactly zero
+//    (all exponents below -160: 2^-160 rounds to 0 in fp32 and bf16) skips
+//    that block's exp2 and PV, which leaves the result bit for bit unchanged;
 //  * workgroups are numbered so that all tiles of one (sequence, KV head) land
 //    on the same XCD (dispatch is round-robin over the 8 XCDs), where they
 //    stream the same K/V blocks through that XCD's L2.
@@ -47,7 +54,15 @@ constexpr int kBlkKeys = 128;     // keys per block (8 pages)
 constexpr int kD = 128;           // head dim
 constexpr int kKBytes = kBlkKeys * kD;          // 16 KB of K rows per block
 constexpr int kVBytes = kBlkKeys * kD;          // 16 KB of V^T per block
-constexpr int kBiasN = 160;                     // bias table entries per wave
+constexpr int kBiasN = 160;                     // bias table entries (distances) of a block
+constexpr int kBiasWave = 736;                  // four copies per wave, one per lane group
+
+// Lane group g reads its own copy of the wave's bias table, starting at entry
+// bias_copy(g). One lookup has the 16 lanes of group g read 16 consecutive
+// entries 32 g below group 0's; the copy bases (0, 208, 400, 576) put the
+// four windows on disjoint banks whether the banks number 32 (two lane groups
+// served together) or 64 (all four), where one shared copy conflicts 2-way.
+__device__ __forceinline__ int bias_copy(int g) { return 192 * g + ((g == 1 || g == 2) ? 16 : 0); }
 constexpr int kLoadChunks = (kKBytes + kVBytes) / 16 / (64 * kPW);  // 16-byte chunks per thread
 
 // Swizzle of the 16-byte column chunks of a K row in LDS. The 16 lanes of one
@@ -64,7 +79,7 @@ struct __align__(16) PrefillSmem {
   uint4 v[2 * kVBytes / 16];    // bf16 V^T: [8 pages][2 halves][128 dims][8 tokens];
                                 // fp8-P variant: e4m3 V^T [8 pages][128 dims][16 tokens]
                                 // in the first half
-  float bias[kPW][kBiasN];      // per wave: bias * log2(e) by distance
+  float bias[kPW][kBiasWave];   // per wave: bias * log2(e) by distance, four copies
 };
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -94,9 +109,14 @@ constexpr int kBiasNone = 0, kBiasSlope = 1, kBiasTable = 2;
 // the invariant log2(448) - 8 = 0.807).
 constexpr float kLazySlack = 0.75f;
 
+// Lazy-rescale slack of the bf16-P path (P <= 2^8), and the exponent gap
+// below the running max past which every P is exactly zero.
+constexpr float kLazyBf16 = 8.0f;
+constexpr float kZeroGap = 160.0f;
+
 template <int kKind, bool kP8>
 __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2)))
-void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blocks) {
+void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blocks, int chunk, int nchunks) {
   __shared__ PrefillSmem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -104,13 +124,18 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
   const int row = lane & 15;
   const int grp = lane >> 4;
 
-  // ---- work item: XCD-major numbering (workgroup i runs on XCD i % 8)
+  // ---- work item (workgroup i runs on XCD i % 8). The tiles of a unit
+  // (sequence, KV head, head block) form nchunks chunks of `chunk` tiles;
+  // (unit, chunk) pairs go round-robin over the XCDs, so with 8 or more tiles
+  // every XCD holds one chunk of every unit (the same mix of units, whatever
+  // their cost), and each chunk's tiles stream the unit's K/V through one L2.
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
   const int slot = bid >> 3;
-  const int u = xcd + 8 * (slot / tiles);
-  const int tile = slot % tiles;
-  if (u >= units) return;
+  const int pair = (slot / chunk) * 8 + xcd;
+  const int u = pair / nchunks;
+  const int tile = (pair - u * nchunks) * chunk + slot % chunk;
+  if (u >= units || tile >= tiles) return;
   const int hb = u % head_blocks;
   const int g = (u / head_blocks) % a.hkv;
   const int b = u / (head_blocks * a.hkv);
@@ -230,12 +255,12 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
   };
 
   const float fold = a.fold_log2;
-  if (blk_lo <= blk_hi) load_block(blk_lo);   // empty when seq_lens < new tokens
-  for (int blk = blk_lo; blk <= blk_hi; ++blk) {
+  if (blk_lo <= blk_hi) load_block(blk_hi);   // empty when seq_lens < new tokens
+  for (int blk = blk_hi; blk >= blk_lo; --blk) {
     __syncthreads();                  // everyone is done reading the previous block
     stash_block(blk);
     __syncthreads();
-    if (blk < blk_hi) load_block(blk + 1);
+    if (blk > blk_lo) load_block(blk - 1);
     const int j0 = blk * kBlkKeys;
 
     // ---- per-wave bias table for this block: entry e <-> distance
@@ -246,13 +271,16 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
     const bool far = kKind == kBiasTable && P0 - (j0 + kBlkKeys - 1) >= a.rel_extent - 1;
     if (kBias && !far) {
       for (int e = lane; e < kBiasN; e += 64) {
+        float val;
         if (kKind == kBiasSlope) {
           const float d = (float)(P0 - j0 + e - 127);
-          sm.bias[wave][e] = round_bf16_finite(slope * -d) * kLog2e;
+          val = round_bf16_finite(slope * -d) * kLog2e;
         } else {
           const int d = min(max(P0 - j0 + e - 127, 0), a.rel_extent - 1);   // later keys are masked
-          sm.bias[wave][e] = __uint_as_float((uint32_t)rel_row[d] << 16) * kLog2e;
+          val = __uint_as_float((uint32_t)rel_row[d] << 16) * kLog2e;
         }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) sm.bias[wave][bias_copy(g) + e] = val;
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -276,13 +304,15 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
     }
     uint4 pk[2][4];     // P in bf16: pk[cb][kk] holds keys 8kk .. 8kk+7 of the lane group
     v8i pk8[2];         // fp8-P variant: byte 4j + i of pk8[cb] is key 32*grp + 4j + i
+    const float scale = kBias ? 1.0f : fold;
+    float xmax[2];      // the block's largest exponent argument of this lane's query row
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       const int r = cb * 16 + row;
       // This lane's keys are j0 + 32*grp + c, c = 16*(j/4) + 4*(j%4) + i in
       // [0, 32). Bias entry r - kidx + 127 = tb_base + (31 - c) with
       // tb_base >= 0, so every lookup is an immediate LDS offset.
-      const float *tb = &sm.bias[wave][r - 32 * grp + 96];
+      const float *tb = &sm.bias[wave][bias_copy(grp) + r - 32 * grp + 96];
       const int c_hi = P0 + r - j0 - 32 * grp;              // keys with c <= c_hi are causal
       const int c_lo = a.window > 0 ? c_hi - a.window : -1;  // and c > c_lo inside the window
       if (kBias && far) {
@@ -313,14 +343,21 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
         for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, s[cb][j][i]);
       bmax = wave_max_xor(bmax, 16);
       bmax = wave_max_xor(bmax, 32);
-      const float scale = kBias ? 1.0f : fold;
+      xmax[cb] = bmax * scale;
+    }
+    // Every P of the block is 2^(x - m) with x <= xmax; when xmax lies more
+    // than kZeroGap below the running max in every row of the wave, all of
+    // them round to zero and PV would add exact zeros: skip the block. (With
+    // no key seen yet, m = -inf and a finite xmax is live.)
+    if (!__ballot(xmax[0] > m_run[0] - kZeroGap || xmax[1] > m_run[1] - kZeroGap)) continue;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
       if constexpr (kP8) {
         // single e4m3 term P = 2^(x - m + 8); the running max is raised (to
         // the block max) only when a score passes it by more than the slack
-        const float xmax = bmax * scale;
-        const bool raise = xmax > m_run[cb] + kLazySlack;
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run[cb] - xmax) : 1.0f;   // 0 from -inf
-        if (raise) m_run[cb] = xmax;
+        const bool raise = xmax[cb] > m_run[cb] + kLazySlack;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run[cb] - xmax[cb]) : 1.0f;   // 0 from -inf
+        if (raise) m_run[cb] = xmax[cb];
         const float off8 = 8.0f - (m_run[cb] == -INFINITY ? 0.0f : m_run[cb]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -336,10 +373,12 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
         }
         continue;
       }
-      const float m_new = fmaxf(m_run[cb], bmax * scale);
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_use);
-      m_run[cb] = m_new;
+      // lazy max: raised (to the block max) only when a score passes it by
+      // more than kLazyBf16, so P <= 2^8
+      const bool raise = xmax[cb] > m_run[cb] + kLazyBf16;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run[cb] - xmax[cb]) : 1.0f;   // 0 from -inf
+      if (raise) m_run[cb] = xmax[cb];
+      const float m_use = m_run[cb] == -INFINITY ? 0.0f : m_run[cb];
       // P = 2^(x - m); pk[cb][kk] = keys 8kk .. 8kk+7 (j = 2kk, 2kk+1), the
       // B-operand slice of PV step kk
 #pragma unroll
@@ -427,17 +466,19 @@ hipError_t launch_prefill_e4m3(const PrefillE4M3Launch &a, hipStream_t s) {
   const int units = a.batch * a.hkv * head_blocks;
   const int tiles = (a.max_q_len + kTileTok - 1) / kTileTok;
   if (tiles == 0) return hipSuccess;
-  const size_t grid = (size_t)8 * ((units + 7) / 8) * tiles;
+  const int chunk = tiles >= 8 ? (tiles + 7) / 8 : tiles;   // tiles per chunk
+  const int nchunks = (tiles + chunk - 1) / chunk;
+  const size_t grid = (size_t)8 * (((size_t)units * nchunks + 7) / 8) * chunk;
   const dim3 g((unsigned)grid), b(64 * kPW);
   const int kind = a.slopes != nullptr ? kBiasSlope : (a.rel != nullptr ? kBiasTable : kBiasNone);
   if (a.fp8_p) {
-    if (kind == kBiasSlope) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasSlope, true>), g, b, 0, s, a, tiles, units, head_blocks);
-    else if (kind == kBiasTable) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasTable, true>), g, b, 0, s, a, tiles, units, head_blocks);
-    else hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasNone, true>), g, b, 0, s, a, tiles, units, head_blocks);
+    if (kind == kBiasSlope) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasSlope, true>), g, b, 0, s, a, tiles, units, head_blocks, chunk, nchunks);
+    else if (kind == kBiasTable) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasTable, true>), g, b, 0, s, a, tiles, units, head_blocks, chunk, nchunks);
+    else hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasNone, true>), g, b, 0, s, a, tiles, units, head_blocks, chunk, nchunks);
   } else {
-    if (kind == kBiasSlope) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasSlope, false>), g, b, 0, s, a, tiles, units, head_blocks);
-    else if (kind == kBiasTable) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasTable, false>), g, b, 0, s, a, tiles, units, head_blocks);
-    else hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasNone, false>), g, b, 0, s, a, tiles, units, head_blocks);
+    if (kind == kBiasSlope) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasSlope, false>), g, b, 0, s, a, tiles, units, head_blocks, chunk, nchunks);
+    else if (kind == kBiasTable) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasTable, false>), g, b, 0, s, a, tiles, units, head_blocks, chunk, nchunks);
+    else hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasNone, false>), g, b, 0, s, a, tiles, units, head_blocks, chunk, nchunks);
   }
   return hipGetLastError();
 }
