@@ -38,6 +38,11 @@
 //    rescaled; and a wave whose every P in a block would be exactly zero
 //    (all exponents below -160: 2^-160 rounds to 0 in fp32 and bf16) skips
 //    that block's exp2 and PV, which leaves the result bit for bit unchanged;
+//    with the slope bias (non-negative slopes) a wave stops altogether once
+//    a bound on every remaining score lies that far below the running max:
+//    |q . k| <= 448 * sum |q| (448 is the e4m3 maximum) and the bias only
+//    falls with distance; the workgroup leaves the key loop when all of its
+//    waves have stopped;
 //  * workgroups are numbered so that all tiles of one (sequence, KV head) land
 //    on the same XCD (dispatch is round-robin over the 8 XCDs), where they
 //    stream the same K/V blocks through that XCD's L2.
@@ -80,6 +85,8 @@ struct __align__(16) PrefillSmem {
                                 // fp8-P variant: e4m3 V^T [8 pages][128 dims][16 tokens]
                                 // in the first half
   float bias[kPW][kBiasWave];   // per wave: bias * log2(e) by distance, four copies
+  int done[2][kPW];             // slope bias: waves whose remaining blocks are all zero P
+  float qbound[kPW][32];        // slope bias: per wave and query row, 448 * sum |q|
 };
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -175,6 +182,27 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
   }
   constexpr bool kBias = kKind != kBiasNone;
   const float slope = kKind == kBiasSlope ? a.slopes[head] : 0.0f;
+  // slope bias: per row, 448 * sum |q| bounds |q . k| in code units (the
+  // margin covers the fp32 sum and the MFMA's accumulation)
+  if constexpr (kKind == kBiasSlope) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(qop[cb][c], false);
+        const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(qop[cb][c], true);
+        acc += (fabsf(lo.x) + fabsf(lo.y)) + (fabsf(hi.x) + fabsf(hi.y));
+      }
+      acc += __shfl_xor(acc, 16, 64);
+      acc += __shfl_xor(acc, 32, 64);
+      if (grp == 0) sm.qbound[wave][cb * 16 + row] = acc * (448.0f * 1.001f);
+    }
+    // read back by every lane group of this wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
   const uint16_t *rel_row = kKind == kBiasTable ? a.rel + (size_t)head * a.rel_extent : nullptr;
   const float rel_last = kKind == kBiasTable ? __uint_as_float((uint32_t)rel_row[a.rel_extent - 1] << 16) * kLog2e : 0.0f;
 
@@ -256,12 +284,37 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
 
   const float fold = a.fold_log2;
   if (blk_lo <= blk_hi) load_block(blk_hi);   // empty when seq_lens < new tokens
+  bool wdone = false;   // slope bias: every P of this wave's remaining blocks is zero
   for (int blk = blk_hi; blk >= blk_lo; --blk) {
+    const int j0 = blk * kBlkKeys;
+    if constexpr (kKind == kBiasSlope) {
+      // the remaining keys are <= j0 + 127: the bias of row r is at most the
+      // one at distance max(0, P0 + r - (j0 + 127)); rows past the tile's
+      // tokens (and waves without a head) are not written and do not count
+      if (!wdone && slope >= 0.0f) {
+        bool ok = true;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          const int r = cb * 16 + row;
+          const int dmin = max(0, P0 + r - (j0 + kBlkKeys - 1));
+          const float ub = fmaf(fold, sm.qbound[wave][r], round_bf16_finite(slope * -(float)dmin) * kLog2e);
+          ok = ok && (!head_ok || r >= ntok || ub < m_run[cb] - kZeroGap);
+        }
+        wdone = __ballot(!ok) == 0;
+      }
+      if (lane == 0) sm.done[blk & 1][wave] = wdone ? 1 : 0;
+    }
     __syncthreads();                  // everyone is done reading the previous block
+    if constexpr (kKind == kBiasSlope) {
+      bool all = true;
+#pragma unroll
+      for (int w = 0; w < kPW; ++w) all = all && sm.done[blk & 1][w] != 0;
+      if (all) break;                 // uniform: every wave reads the same flags
+    }
     stash_block(blk);
     __syncthreads();
     if (blk > blk_lo) load_block(blk - 1);
-    const int j0 = blk * kBlkKeys;
+    if (kKind == kBiasSlope && wdone) continue;
 
     // ---- per-wave bias table for this block: entry e <-> distance
     // d = (P0 - j0) + e - 127, value bf16(slope * -d) or T[min(d, E - 1)],

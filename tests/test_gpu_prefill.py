@@ -3,6 +3,8 @@ import numpy as np
 import pytest
 import torch
 
+import fp4_quantized_paged_amd as kvq
+
 from oracle.attention import paged_prefill
 from workloads import config_chunked_prefill, make_attn_case, geometric_slopes
 from parity import DeviceCase, oracle_scales, oracle_cache, seq_tokens, check_attention
@@ -145,3 +147,37 @@ def test_chunked_prefill_fp8_p_full_size_sampled():
         rows += list(r0 + np.unique(picks))
     _, out, ref = run_case(c, rows=rows, seqs=[1, 3], fp8_p=True)
     print(check_fp8_p(out, ref, "chunked_prefill fp8 P"))
+
+
+def slope_table(slopes, extent):
+    """The slope bias written out as a learned table: T[h][d] = bf16(fp32(slope_h) * fp32(-d))."""
+    d = -np.arange(extent, dtype=np.float32)
+    prod = (np.asarray(slopes, dtype=np.float32)[:, None] * d[None, :]).astype(np.float32)
+    return torch.from_numpy(prod).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("fp8_p", [False, True])
+@pytest.mark.parametrize("which", ["small", "full"])
+def test_prefill_slope_early_stop_is_exact(which, fp8_p):
+    """With the slope bias a wave stops once a bound puts every remaining
+    probability at exactly zero, and both bias kinds skip blocks whose every P
+    is zero. The learned-table path, given a table holding the same bf16
+    biases with an extent past every distance, never stops early: the two
+    outputs are equal bit for bit, on a small case and on the full
+    4 x (32,768 + 2,048) launch."""
+    if which == "full":
+        c = config_chunked_prefill()
+    else:
+        c = make_attn_case("pstop", 77, [4096, 3000, 700], [200, 77, 700], 32, 4, 128,
+                           v_std=2.0, slopes=geometric_slopes(32))
+    dc = DeviceCase(c)
+    s = dc.calibrate()
+    dc.store_all(s)
+    a = dc.prefill(s, fp8_p=fp8_p)
+    tab = slope_table(c.slopes, c.max_seq_len).cuda()
+    b = kvq.prefill(dc.cache, dc.q, dc.cu_q_lens, c.max_q_len, dc.block_table, dc.seq_lens,
+                    c.max_seq_len, c.softmax_scale, s["q"], s["k"], s["v"], c.window, None,
+                    rel_bias=tab, fp8_p=fp8_p)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(a.float()))
+    assert torch.equal(a, b)
