@@ -430,7 +430,9 @@ def nvfp4_prefill_rows(torch, kvq):
 
 def prefill_flops(seq_lens, q_lens, Hq, D, window=0):
     """QK^T and PV multiply-adds of causal chunked prefill, 2 flops each:
-    4 * D per attended (query row, head, key)."""
+    4 * D per attended (query row, head, key). Nominal: every causal pair
+    counts, also those whose probability is exactly zero under the bias,
+    whose work the kernel skips."""
     visits = 0
     for L, lq in zip(seq_lens, q_lens):
         pos = np.arange(L - lq, L, dtype=np.int64)
@@ -473,10 +475,17 @@ def prefill_rows(torch, kvq):
     ms_p8 = timed_mean(torch, lambda: kvq.prefill(cache, q, cu, c.max_q_len, bt, sl, c.max_seq_len,
                                                   c.softmax_scale, sc["q"], sc["k"], sc["v"],
                                                   slopes=slopes, out=out, fp8_p=True), reps=5)
+    # the same prefill without a bias: no probability underflows, every block
+    # is computed (the dense rate of the kernel)
+    ms_nb = timed_mean(torch, lambda: kvq.prefill(cache, q, cu, c.max_q_len, bt, sl, c.max_seq_len,
+                                                  c.softmax_scale, sc["q"], sc["k"], sc["v"], out=out), reps=5)
     T = int(kn.shape[0])
     del cache
     torch.cuda.empty_cache()
-    return {"chunked_prefill": {"batch": c.batch, "new_tokens": int(c.q_lens[0]),
+    return {"chunked_prefill_nobias": {"us": round(ms_nb * 1e3, 1),
+                                       "TFLOP_s": round(fl / (ms_nb * 1e-3) / 1e12, 1),
+                                       "pct_of_fp8_peak": round(100 * fl / (ms_nb * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 2)},
+            "chunked_prefill": {"batch": c.batch, "new_tokens": int(c.q_lens[0]),
                                 "context": c.max_seq_len, "us": round(ms * 1e3, 1),
                                 "TFLOP_s": round(tf, 1), "flops": fl,
                                 "pct_of_fp8_peak": round(100 * tf / FP8_PEAK_TFLOPS, 2)},
