@@ -286,16 +286,19 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   v4h pb_prev = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};   // P of the previous page
 
   // K rows, chunk-major: 16-byte chunk ch (dims 8ch .. 8ch+7 of the wave's
-  // 256) of key r sits at 256*ch + 16*(r ^ 4*(ch&1)). Row writes (8 lanes =
-  // 8 keys of one chunk) and transposed reads (16 lanes = 4 keys x 2 chunks)
-  // both cover 32 distinct banks. Buffer j of the wave is kKtBytes further.
+  // 256) of key r sits at 256*ch + 16*(r ^ 8*(ch&1)). Row writes (8 or 16
+  // keys of one chunk) cover distinct banks; a transposed read serves 32
+  // lanes (keys 0-7 or 8-15 of chunks 2q and 2q+1) per pass, and the XOR
+  // puts the odd chunk's half of them in the other 128 bytes, so the pass
+  // covers all 64 banks once (XOR 4 had left both chunks' keys on the same
+  // 32 banks, a 2-way conflict). Buffer j of the wave is kKtBytes further.
   uint8_t *kt = smem + wave * 2 * kKtBytes;
   uint8_t *wbase_e = kt + 2048 * grp + 16 * row;          // even steps: chunk 8*grp + c
-  uint8_t *wbase_o = kt + 2048 * grp + 16 * (row ^ 4);    // odd steps
+  uint8_t *wbase_o = kt + 2048 * grp + 16 * (row ^ 8);    // odd steps
   // transposed reads: lane s of group grp reads key 4*grp + s/4, dims
   // 16q + 4(s%4) .. +4 = chunk 2q + (s%4)/2, 8-byte half (s%4)&1
   const int rc1 = (row & 3) >> 1;
-  const uint8_t *rbase = kt + 256 * rc1 + 16 * ((4 * grp + (row >> 2)) ^ (4 * rc1)) + 8 * (row & 1);
+  const uint8_t *rbase = kt + 256 * rc1 + 16 * ((4 * grp + (row >> 2)) ^ (8 * rc1)) + 8 * (row & 1);
   v4f *xch = (v4f *)(smem + kXchOff) + pair * 2 * 2 * 64;   // [buf][half][lane]
   uint8_t *st_nib = kt + kStageNib * (lane >> 3) + 16 * (lane & 7);          // + 8*kStageNib for load 1
   uint8_t *st_tail = kt + kStageTail + kStageTailRow * (lane >> 2) + 16 * tch;
