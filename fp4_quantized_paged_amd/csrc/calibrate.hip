@@ -39,15 +39,16 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(AmaxLaunch a) {
   const int64_t cpr = a.row_len >> 3;
   const int64_t nwaves = (int64_t)gridDim.x * kAmaxWaves;
   uint32_t m = 0;
-  int64_t r = (int64_t)blockIdx.x * kAmaxWaves + wave;
-  // kRowUnroll rows per iteration keep several loads per lane in flight
+  int64_t r = ((int64_t)blockIdx.x * kAmaxWaves + wave) * kRowUnroll;
+  // each wave takes kRowUnroll consecutive rows per iteration (a workgroup
+  // reads one contiguous span), several loads per lane in flight
   for (; r < a.rows; r += nwaves * kRowUnroll) {
     uint4 x[kRowUnroll];
     bool keep[kRowUnroll];
     for (int64_t c = lane; c < cpr; c += 64) {
 #pragma unroll
       for (int u = 0; u < kRowUnroll; ++u) {
-        const int64_t rr = r + u * nwaves;
+        const int64_t rr = r + u;
         keep[u] = rr < a.rows && (a.slot == nullptr || a.slot[rr] >= 0);
         if (keep[u]) {
           const v4u w = __builtin_nontemporal_load((const v4u *)(a.x + rr * a.row_stride + (c << 3)));
@@ -108,14 +109,14 @@ __global__ __launch_bounds__(kAmaxThreads) void band_kernel(BandLaunch a) {
   const int64_t cpr = a.row_len >> 3;
   const int64_t nwaves = (int64_t)gridDim.x * kAmaxWaves;
   uint32_t n_clip = 0, n_flush = 0;
-  int64_t r = (int64_t)blockIdx.x * kAmaxWaves + wave;
+  int64_t r = ((int64_t)blockIdx.x * kAmaxWaves + wave) * kRowUnroll;
   for (; r < a.rows; r += nwaves * kRowUnroll) {
     for (int64_t c = lane; c < cpr; c += 64) {
       uint4 x[kRowUnroll];
       bool keep[kRowUnroll];
 #pragma unroll
       for (int u = 0; u < kRowUnroll; ++u) {
-        const int64_t rr = r + u * nwaves;
+        const int64_t rr = r + u;
         keep[u] = rr < a.rows && (a.slot == nullptr || a.slot[rr] >= 0);
         if (keep[u]) {
           const v4u w = __builtin_nontemporal_load((const v4u *)(a.x + rr * a.row_stride + (c << 3)));
@@ -167,8 +168,10 @@ __global__ __launch_bounds__(kAmaxThreads) void band_kernel(BandLaunch a) {
 
 hipError_t launch_amax(const AmaxLaunch &a, int num_cus, hipStream_t s) {
   if (a.rows > 0) {
+    // one resident round (8 workgroups = 32 waves per CU) streams best for
+    // this load-only kernel; a second round left a tail
     int64_t blocks = (a.rows + kAmaxWaves * kRowUnroll - 1) / (kAmaxWaves * kRowUnroll);
-    const int64_t cap = (int64_t)num_cus * 16;
+    const int64_t cap = (int64_t)num_cus * 8;
     if (blocks > cap) blocks = cap;
     hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, s, a);
     hipError_t e = hipGetLastError();
