@@ -168,10 +168,11 @@ __global__ __launch_bounds__(kAmaxThreads) void band_kernel(BandLaunch a) {
 
 hipError_t launch_amax(const AmaxLaunch &a, int num_cus, hipStream_t s) {
   if (a.rows > 0) {
-    // one resident round (8 workgroups = 32 waves per CU) streams best for
-    // this load-only kernel; a second round left a tail
+    // a load-only stream: 4 workgroups (16 waves) per CU with four 16-byte
+    // loads per lane in flight measured fastest (more waves, or a second
+    // round of workgroups, streamed slower)
     int64_t blocks = (a.rows + kAmaxWaves * kRowUnroll - 1) / (kAmaxWaves * kRowUnroll);
-    const int64_t cap = (int64_t)num_cus * 8;
+    const int64_t cap = (int64_t)num_cus * 4;
     if (blocks > cap) blocks = cap;
     hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, s, a);
     hipError_t e = hipGetLastError();
