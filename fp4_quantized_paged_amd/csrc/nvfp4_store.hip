@@ -20,9 +20,11 @@
 // group-scale codes; [288,292) zero; [292,296) s2 (little endian);
 // [296,304) zero; [304,368) RoPE codes.
 //
-// One 32-lane half of a wave handles one token, one lane per 16-element group
-// (plus two RoPE elements per lane). The record is assembled in LDS and
-// leaves as 23 16-byte stores; the 16 records of a page are contiguous.
+// One 32-lane half of a wave handles one token per pass, one lane per
+// 16-element group (plus two RoPE elements per lane); the loads of both
+// passes are issued before either token is encoded. The records are assembled
+// in LDS and leave as 23 16-byte stores each, with the slots kept in LDS; the
+// 16 records of a workgroup (a whole page in a bulk store) are contiguous.
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -33,8 +35,10 @@ namespace kvq {
 namespace {
 
 constexpr int kRec = 368;
-constexpr int kTokensPerBlock = 8;        // 4 waves x 2 tokens
 constexpr int kThreads = 256;
+constexpr int kHalves = kThreads / 32;    // half waves: one token each per pass
+constexpr int kPasses = 2;                // tokens per half wave (1 and 4 measured slower)
+constexpr int kTokensPerBlock = kHalves * kPasses;
 
 // e2m1 code (0..7) of a magnitude already clipped to [0, 6], round to nearest
 // even code: the grid is evenly spaced inside each binade, so rint on the
@@ -52,26 +56,9 @@ __device__ __forceinline__ uint32_t e2m1_encode(float y) {
   return e2m1_code(a) | ((__float_as_uint(y) >> 28) & 8u);   // sign bit kept
 }
 
-__global__ __launch_bounds__(kThreads) void store_nvfp4_kernel(StoreNvfp4Launch a) {
-  __shared__ __align__(16) uint8_t rec[kTokensPerBlock][kRec];
-  const int tid = threadIdx.x;
-  const int half = tid >> 5;                 // token within the block
-  const int g = tid & 31;                    // latent group / RoPE pair
-  const int64_t t = (int64_t)blockIdx.x * kTokensPerBlock + half;
-  const bool live = t < a.num_tokens;
-  const int64_t slot = live ? a.slot[t] : -1;
-
-  // ---- load this lane's 16 latent elements and 2 RoPE elements
-  uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-  uint32_t rp = 0;
-  if (slot >= 0) {
-    const uint16_t *src = a.x + t * a.stride;
-    const v4u w0 = __builtin_nontemporal_load((const v4u *)(src + 16 * g));
-    const v4u w1 = __builtin_nontemporal_load((const v4u *)(src + 16 * g + 8));
-    x0 = make_uint4(w0.x, w0.y, w0.z, w0.w);
-    x1 = make_uint4(w1.x, w1.y, w1.z, w1.w);
-    rp = *(const uint32_t *)(src + 512 + 2 * g);
-  }
+// One token's record, from its already loaded elements, into LDS.
+__device__ __forceinline__ void encode_token(const StoreNvfp4Launch &a, uint4 x0, uint4 x1, uint32_t rp, int g,
+                                             uint8_t *R) {
   const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 
   // ---- group amax (|bf16| orders like its bits), token amax over 32 lanes
@@ -110,8 +97,7 @@ __global__ __launch_bounds__(kThreads) void store_nvfp4_kernel(StoreNvfp4Launch 
                                                                   sat448(bf16hi(rp) * a.rope_inv), 0, false) &
                         0xFFFFu;
 
-  // ---- assemble the record in LDS
-  uint8_t *R = rec[half];
+  // ---- the record in LDS
   *(uint2 *)(R + 8 * g) = make_uint2(packed[0], packed[1]);
   R[256 + g] = (uint8_t)sg;
   *(uint16_t *)(R + 304 + 2 * g) = (uint16_t)rope;
@@ -120,15 +106,44 @@ __global__ __launch_bounds__(kThreads) void store_nvfp4_kernel(StoreNvfp4Launch 
     *(float *)(R + 292) = s2;
     *(uint2 *)(R + 296) = make_uint2(0u, 0u);
   }
+}
+
+__global__ __launch_bounds__(kThreads) void store_nvfp4_kernel(StoreNvfp4Launch a) {
+  __shared__ __align__(16) uint8_t rec[kTokensPerBlock][kRec];
+  __shared__ int64_t sslot[kTokensPerBlock];   // the records' slots, for the store phase
+  const int tid = threadIdx.x;
+  const int half = tid >> 5;                 // token slot within a pass
+  const int g = tid & 31;                    // latent group / RoPE pair
+  const int64_t tb = (int64_t)blockIdx.x * kTokensPerBlock;
+
+  // ---- every pass's loads first (the half wave's tokens half, half + 8, ...)
+  uint4 x0[kPasses], x1[kPasses];
+  uint32_t rp[kPasses];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int64_t t = tb + p * kHalves + half;
+    const int64_t slot = t < a.num_tokens ? a.slot[t] : -1;
+    if (g == 0) sslot[p * kHalves + half] = slot;
+    x0[p] = x1[p] = make_uint4(0, 0, 0, 0);
+    rp[p] = 0;
+    if (slot >= 0) {
+      const uint16_t *src = a.x + t * a.stride;
+      const v4u w0 = __builtin_nontemporal_load((const v4u *)(src + 16 * g));
+      const v4u w1 = __builtin_nontemporal_load((const v4u *)(src + 16 * g + 8));
+      x0[p] = make_uint4(w0.x, w0.y, w0.z, w0.w);
+      x1[p] = make_uint4(w1.x, w1.y, w1.z, w1.w);
+      rp[p] = *(const uint32_t *)(src + 512 + 2 * g);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) encode_token(a, x0[p], x1[p], rp[p], g, rec[p * kHalves + half]);
   __syncthreads();
 
   // ---- 23 16-byte stores per record
   for (int c = tid; c < kTokensPerBlock * (kRec / 16); c += kThreads) {
     const int tok = c / (kRec / 16);
     const int part = c - tok * (kRec / 16);
-    const int64_t tt = (int64_t)blockIdx.x * kTokensPerBlock + tok;
-    if (tt >= a.num_tokens) continue;
-    const int64_t s = a.slot[tt];
+    const int64_t s = sslot[tok];   // -1 past the last token and for skipped tokens
     if (s < 0) continue;
     const v4u v = *(const v4u *)(rec[tok] + 16 * part);
     __builtin_nontemporal_store(v, (v4u *)(a.records + (size_t)s * kRec + 16 * part));
