@@ -19,9 +19,9 @@
 //    pre-scaled per head by a power of two that puts its largest element in
 //    [2^13, 2^14) (exact for all but elements 2^-31 below the head maximum);
 //  * QK^T on v_mfma_f32_16x16x32_f16 (A = 16 keys x 32 dims from registers,
-//    B = the 16 heads). The two half-dot-products meet through LDS (one
-//    workgroup barrier per page); both waves then run the same softmax on
-//    identical scores;
+//    B = the 16 heads). The two half-dot-products meet through LDS (a
+//    handshake of the pair's two waves per page, no workgroup barrier);
+//    both waves then run the same softmax on identical scores;
 //  * the dequantized rows also go to LDS (chunk-major, bank-conflict free,
 //    two buffers per wave) and PV (v_mfma_f32_16x16x16_f16, A = V^T) reads
 //    them back with ds_read_b64_tr_b16, whose 16-lane transpose turns four
@@ -64,7 +64,7 @@ constexpr int kGUnset = -(1 << 20);               // Gs before any nonzero outer
 constexpr int kSlabRow = kHalf + 4;               // merge slab row (floats, padded)
 constexpr int kBtPerThread = 4;                   // block-table entries staged per thread
 constexpr int kMaxSplitPages = kBtPerThread * kThreads;   // pages of one split (2,048)
-constexpr int kBufs = 4;                          // pages of record bytes in flight per wave
+constexpr int kBufs = 4;                          // pages of record bytes in flight per wave (5 or 6: slower)
 
 // LDS: two K-row buffers per wave, then the pair exchange. Before the loop
 // the first region holds the staged bf16 Q; after it, the merge slabs.
@@ -147,6 +147,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   __shared__ __align__(16) uint8_t smem[kSmemBytes];
   __shared__ float s_m[kPairs][kHeads], s_l[kPairs][kHeads], s_e[kPairs][kHeads];
   __shared__ int s_k[kHeads];
+  __shared__ int s_flag[kPairs][2];                    // pages whose half scores are published
   __shared__ int s_bt[kMaxSplitPages];                 // this split's block-table slice
 
   const int lane = threadIdx.x & 63;
@@ -206,17 +207,12 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   };
   // The first four page slots are requested before the Q work (page ids
   // from the wave's own copy), so that their latency overlaps Q's.
-  PageRaw buf0, buf1, buf2, buf3;
-  {
-    auto first = [&](int k, PageRaw &r) {
-      const int p = p_begin + pair + k * kPairs;
-      const int ph = __builtin_amdgcn_readlane(btw, pair + k * kPairs);   // a clamped copy past the split
-      fetch_from(p < p_end ? a.records + (size_t)ph * (16 * kRec) : dummy, r);
-    };
-    first(0, buf0);
-    first(1, buf1);
-    first(2, buf2);
-    first(3, buf3);
+  PageRaw bufs[kBufs];
+#pragma unroll
+  for (int k = 0; k < kBufs; ++k) {
+    const int p = p_begin + pair + k * kPairs;
+    const int ph = __builtin_amdgcn_readlane(btw, pair + k * kPairs);   // a clamped copy past the split
+    fetch_from(p < p_end ? a.records + (size_t)ph * (16 * kRec) : dummy, bufs[k]);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -269,6 +265,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     // K-row buffers start at zero: the PV of a page slot that holds no page
     // multiplies them by P = 0
     for (int c = threadIdx.x; c < kXchOff / 16; c += kThreads) ((uint4 *)smem)[c] = make_uint4(0, 0, 0, 0);
+    if (threadIdx.x < 2 * kPairs) (&s_flag[0][0])[threadIdx.x] = 0;
     __syncthreads();
   }
   const float c_score = __builtin_ldexpf(a.scale_log2, -s_k[row]);   // undoes 2^k of head `row`
@@ -305,6 +302,21 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   const uint8_t *ld_nib = kt + kStageNib * row + 32 * grp;
   const uint8_t *ld_tail = kt + kStageTail + kStageTailRow * row;
 
+  // Pair handshake: the exchange slots and K-row buffers are the pair's own,
+  // so only the two waves of a pair meet per page. Each wave publishes a
+  // page counter after its half scores and waits for its partner's; LDS
+  // operations of one wave complete in issue order, so a counter that reads
+  // n means the partner's scores of page n are in place. Both waves write
+  // before they wait and run the same number of pages, so every wait ends.
+  typedef __attribute__((address_space(3))) volatile int lds_int;
+  lds_int *my_flag = (lds_int *)&s_flag[pair][half];
+  lds_int *their_flag = (lds_int *)&s_flag[pair][half ^ 1];
+  auto pair_sync = [&](int n) {
+    __asm__ volatile("" ::: "memory");
+    if (lane == 0) *my_flag = n;
+    while (*their_flag < n) __builtin_amdgcn_s_sleep(1);
+    __asm__ volatile("" ::: "memory");
+  };
   auto fetch = [&](int p, PageRaw &r) {
     fetch_from(p < p_end ? a.records + (size_t)__builtin_amdgcn_readfirstlane(s_bt[p - p_begin]) * (16 * kRec) : dummy,
                r);
@@ -396,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
       s2p[i] = __builtin_ldexpf(op.s2k[i], -Gs);   // < 1
     }
     xch[(k & 1) * 128 + half * 64 + lane] = y;
-    __syncthreads();
+    pair_sync(k + 1);
     // ---- next slot's bytes: staged into buffer (k+1)&1 (the PV above was
     // its last reader); its load buffer is refilled right away
     stage(raw, pbuf, op);
@@ -442,18 +454,17 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
 
   const int iters = p_end > p_begin ? (p_end - p_begin + kPairs - 1) / kPairs : 0;
   PageOp op;
-  stage(buf0, 0, op);   // slot 0 into K-row buffer 0
-  fetch(p_begin + pair + kBufs * kPairs, buf0);
+  stage(bufs[0], 0, op);   // slot 0 into K-row buffer 0
+  fetch(p_begin + pair + kBufs * kPairs, bufs[0]);
+  // slot k sits in load buffer k % kBufs; step k stages slot k + 1
   int it = 0;
-  for (; it + 3 < iters; it += 4) {
-    step(op, it, buf1);
-    step(op, it + 1, buf2);
-    step(op, it + 2, buf3);
-    step(op, it + 3, buf0);
+  for (; it + kBufs - 1 < iters; it += kBufs) {
+#pragma unroll
+    for (int j = 0; j < kBufs; ++j) step(op, it + j, bufs[(j + 1) % kBufs]);
   }
-  if (it < iters) step(op, it, buf1);
-  if (it + 1 < iters) step(op, it + 1, buf2);
-  if (it + 2 < iters) step(op, it + 2, buf3);
+#pragma unroll
+  for (int j = 0; j < kBufs - 1; ++j)
+    if (it + j < iters) step(op, it + j, bufs[(j + 1) % kBufs]);
   // PV of the last page slot (K-row buffer (iters - 1) & 1; P is zero if
   // that slot held no page or there was none)
   {
