@@ -552,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
 // Split combine: per (sequence, head), out = 2^(E - M) * sum_s 2^(E_s - E) O_s
 // / sum_s 2^(M_s - M) den_s. Splits that saw no key (M_s = -inf, den_s = 0)
 // and splits with no nonzero term (E_s = -inf) drop out. One thread per 4
-// dims; every split's partial is requested before any is used.
+// dims; the first splits' partials are requested with the split statistics.
 constexpr int kCombineThreads = kLat / 4;
 constexpr int kMaxCombineSplits = 64;
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const float *part_o, const float *part_ml,
@@ -562,6 +562,14 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const floa
   const int bh = blockIdx.x;
   const int t = threadIdx.x;
   const float *ml = part_ml + (size_t)bh * splits * 4;
+  const float *po = part_o + (size_t)bh * splits * kLat + 4 * t;
+  // the first kPre splits' partials are requested together with the split
+  // statistics (one memory round trip); clamped copies past the last split
+  // are not used
+  constexpr int kPre = 8;
+  v4f pre[kPre];
+#pragma unroll
+  for (int s = 0; s < kPre; ++s) pre[s] = *(const v4f *)(po + (size_t)min(s, splits - 1) * kLat);
   if (t < 64) {
     float M = -INFINITY, E = -INFINITY;
     const v4f r = t < splits ? *(const v4f *)(ml + 4 * t) : v4f{-INFINITY, 0.f, -INFINITY, 0.f};
@@ -584,9 +592,11 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const floa
     if (t == 0) s_f = (den > 0.0f && E != -INFINITY) ? __builtin_ldexpf(1.0f / den, (int)(E - M)) : 0.0f;
   }
   __syncthreads();
-  const float *po = part_o + (size_t)bh * splits * kLat + 4 * t;
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < splits; ++s) acc += s_w[0][s] * *(const v4f *)(po + (size_t)s * kLat);
+#pragma unroll
+  for (int s = 0; s < kPre; ++s)
+    if (s < splits) acc += s_w[0][s] * pre[s];
+  for (int s = kPre; s < splits; ++s) acc += s_w[0][s] * *(const v4f *)(po + (size_t)s * kLat);
   const float f = s_f;
   uint2 w;
   w.x = f32_to_bf16_bits(acc[0] * f) | (f32_to_bf16_bits(acc[1] * f) << 16);
