@@ -304,16 +304,23 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
 
   // Pair handshake: the exchange slots and K-row buffers are the pair's own,
   // so only the two waves of a pair meet per page. Each wave publishes a
-  // page counter after its half scores and waits for its partner's; LDS
-  // operations of one wave complete in issue order, so a counter that reads
-  // n means the partner's scores of page n are in place. Both waves write
-  // before they wait and run the same number of pages, so every wait ends.
+  // page counter after its half scores of an active slot and, one step
+  // later, waits for its partner's counter of that slot; LDS operations of
+  // one wave complete in issue order, so a counter that reads n means the
+  // partner's scores of slot n - 1 are in place. Both waves run the same
+  // slots and publish slot j before they wait for slot j, so every wait
+  // ends. A wave overwrites the exchange slot of j only late in slot j + 2,
+  // after waiting (early in slot j + 2) for the partner's counter j + 2,
+  // which the partner publishes late in its slot j + 1, after its reads of
+  // slot j early in that slot.
   typedef __attribute__((address_space(3))) volatile int lds_int;
   lds_int *my_flag = (lds_int *)&s_flag[pair][half];
   lds_int *their_flag = (lds_int *)&s_flag[pair][half ^ 1];
-  auto pair_sync = [&](int n) {
+  auto pair_publish = [&](int n) {
     __asm__ volatile("" ::: "memory");
     if (lane == 0) *my_flag = n;
+  };
+  auto pair_wait = [&](int n) {
     while (*their_flag < n) __builtin_amdgcn_s_sleep(1);
     __asm__ volatile("" ::: "memory");
   };
@@ -337,88 +344,14 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     for (int i = 0; i < 4; ++i) op.s2k[i] = *(const float *)(kt + kb + kStageTail + kStageTailRow * (4 * grp + i) + 20);
   };
 
-  // Page slot k of this pair (page p = p_begin + pair + k*kPairs, if below
-  // p_end): dequant + QK^T of page k (bytes in `op`) into K-row buffer k&1,
-  // interleaved with the PV of page k-1 from the other buffer; exchange of
-  // the half scores; then, while the softmax of page k runs, the bytes of
-  // slot k+1 (`raw`) are staged into the other buffer into `op`, and `raw`
-  // is refilled with slot k+1+kBufs.
-  auto step = [&](PageOp &op, int k, PageRaw &raw) {
-    const int p = p_begin + pair + k * kPairs;
-    const bool active = p < p_end;        // uniform over the wave
-    const bool tail = (p + 1) * 16 > L;   // the sequence's last, partial page
-    const int cb = (k & 1) * kKtBytes;    // this page's K-row buffer
-    const int pbuf = kKtBytes - cb;       // the previous page's, and the next's
-    // Keys past the end, and every key of a slot without a page: group
-    // scales (possibly NaN codes) and outer scales become zero, so their K
-    // rows, V rows and P entries are exactly zero; their scores are masked.
-    if (!active || tail) {
-      if (!active || p * 16 + row >= L) {
-        op.sc = 0u;
-        op.s2 = 0.0f;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (!active || p * 16 + 4 * grp + i >= L) op.s2k[i] = 0.0f;
-    }
-    // ---- outer-scale exponent of the pair (both waves see the same keys);
-    // a raise rescales the accumulator after the previous page's PV
-    const int e2 = __builtin_amdgcn_frexp_expf(op.s2);
-    int g_new = Gs;
-    if (__ballot(op.s2 > 0.0f && e2 > Gs)) {
-      int emax = op.s2 > 0.0f ? e2 : kGUnset;
-#pragma unroll
-      for (int msk = 1; msk < 16; msk <<= 1) emax = max(emax, __shfl_xor(emax, msk, 64));
-      g_new = __builtin_amdgcn_readfirstlane(emax);
-    }
-    // ---- dequant + QK^T of this page, PV of the previous page
-    const v2h sg01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(op.sc, 1.0f, false);
-    const v2h sg23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(op.sc, 1.0f, true);
-    v4f acc_l = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const _Float16 s = (c >> 2) == 0 ? sg01[(c >> 1) & 1] : sg23[(c >> 1) & 1];
-      const uint4 x = fp4x8_f16(op.nib[c >> 2][c & 3], v2h{s, s});
-      *(uint4 *)(((c & 1) ? wbase_o : wbase_e) + cb + 256 * c) = x;
-      acc_l = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, x), __builtin_bit_cast(v8h, qop[c]),
-                                                     acc_l, 0, 0, 0);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int q = 2 * c + j;   // PV tile: dims 16q .. 16q+15
-        const v4s va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s *)(rbase + pbuf + 512 * q));
-        o[q] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h, va), pb_prev, o[q], 0, 0, 0);
-      }
-    }
-    const uint4 xr = e4m3x8_f16(op.rp);
-    const v4f acc_r = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xr), __builtin_bit_cast(v8h, qrope),
-                                                             v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-    if (g_new != Gs) {
-      const float f = __builtin_ldexpf(1.0f, max(Gs - g_new, -200));
-#pragma unroll
-      for (int q = 0; q < 16; ++q) o[q] *= f;
-      Gs = g_new;
-    }
-    // this wave's part of the log2-domain scores of keys 4*grp + i, head `row`
-    v4f y;
-    float s2p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      y[i] = fmaf(c_score * op.s2k[i], acc_l[i], c_rope * acc_r[i]);
-      s2p[i] = __builtin_ldexpf(op.s2k[i], -Gs);   // < 1
-    }
-    xch[(k & 1) * 128 + half * 64 + lane] = y;
-    pair_sync(k + 1);
-    // ---- next slot's bytes: staged into buffer (k+1)&1 (the PV above was
-    // its last reader); its load buffer is refilled right away
-    stage(raw, pbuf, op);
-    fetch(p + (kBufs + 1) * kPairs, raw);
-
-    // ---- softmax of keys 4*grp + i for head `row` (identical in both waves)
-    pb_prev = v4h{(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
-    if (!active) return;
-    const v4f y0 = xch[(k & 1) * 128 + lane];
-    const v4f y1 = xch[(k & 1) * 128 + 64 + lane];
+  // Softmax of page slot j (page p), one page later than its QK^T: the
+  // partner's half scores of slot j were published a whole step earlier, so
+  // the wait for them almost never stalls. Sets pb_prev = P of slot j.
+  auto softmax_of = [&](int j, int p, const float (&s2p)[4]) {
+    const bool tail = (p + 1) * 16 > L;
+    pair_wait(j + 1);
+    const v4f y0 = xch[(j & 1) * 128 + lane];
+    const v4f y1 = xch[(j & 1) * 128 + 64 + lane];
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = y0[i] + y1[i];
@@ -452,6 +385,99 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     pb_prev = v4h{(_Float16)pw[0], (_Float16)pw[1], (_Float16)pw[2], (_Float16)pw[3]};
   };
 
+  // Page slot k of this pair (page p = p_begin + pair + k*kPairs, if below
+  // p_end): the softmax of slot k-1; dequant + QK^T of page k (bytes in `op`)
+  // into K-row buffer k&1, interleaved with the PV of page k-1 from the other
+  // buffer; this wave's half scores of page k published for the partner; then
+  // the bytes of slot k+1 (`raw`) are staged into the other buffer into `op`,
+  // and `raw` is refilled with slot k+1+kBufs. Slots past p_end come last and
+  // publish nothing (neither wave of the pair reads their scores).
+  float s2p_prev[4] = {0.f, 0.f, 0.f, 0.f};   // P scales of slot k-1
+  auto step = [&](PageOp &op, int k, PageRaw &raw) {
+    const int p = p_begin + pair + k * kPairs;
+    const bool active = p < p_end;        // uniform over the wave
+    const bool tail = (p + 1) * 16 > L;   // the sequence's last, partial page
+    const int cb = (k & 1) * kKtBytes;    // this page's K-row buffer
+    const int pbuf = kKtBytes - cb;       // the previous page's, and the next's
+    pb_prev = v4h{(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
+    if (k > 0 && p - kPairs < p_end) softmax_of(k - 1, p - kPairs, s2p_prev);
+    // Keys past the end, and every key of a slot without a page: group
+    // scales (possibly NaN codes) and outer scales become zero, so their K
+    // rows, V rows and P entries are exactly zero; their scores are masked.
+    if (!active || tail) {
+      if (!active || p * 16 + row >= L) {
+        op.sc = 0u;
+        op.s2 = 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!active || p * 16 + 4 * grp + i >= L) op.s2k[i] = 0.0f;
+    }
+    // ---- outer-scale exponent of the pair (both waves see the same keys);
+    // a raise rescales the accumulator after the previous page's PV
+    const int e2 = __builtin_amdgcn_frexp_expf(op.s2);
+    int g_new = Gs;
+    if (__ballot(op.s2 > 0.0f && e2 > Gs)) {
+      int emax = op.s2 > 0.0f ? e2 : kGUnset;
+#pragma unroll
+      for (int msk = 1; msk < 16; msk <<= 1) emax = max(emax, __shfl_xor(emax, msk, 64));
+      g_new = __builtin_amdgcn_readfirstlane(emax);
+    }
+    // ---- dequant + QK^T of this page, PV of the previous page
+    const v2h sg01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(op.sc, 1.0f, false);
+    const v2h sg23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(op.sc, 1.0f, true);
+    v4f acc_l = v4f{0.f, 0.f, 0.f, 0.f};
+    // PV operand reads run kLook tiles ahead of their MFMAs (2, 8 and 16
+    // measured within 1% of each other)
+    constexpr int kLook = 8;
+    v4s va[16];
+    auto read_tile = [&](int q) {
+      va[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(rbase + pbuf + 512 * q));
+    };
+#pragma unroll
+    for (int q = 0; q < kLook; ++q) read_tile(q);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (2 * c + j + kLook < 16) read_tile(2 * c + j + kLook);
+      const _Float16 s = (c >> 2) == 0 ? sg01[(c >> 1) & 1] : sg23[(c >> 1) & 1];
+      const uint4 x = fp4x8_f16(op.nib[c >> 2][c & 3], v2h{s, s});
+      *(uint4 *)(((c & 1) ? wbase_o : wbase_e) + cb + 256 * c) = x;
+      acc_l = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, x), __builtin_bit_cast(v8h, qop[c]),
+                                                     acc_l, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int q = 2 * c + j;   // PV tile: dims 16q .. 16q+15
+        o[q] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h, va[q]), pb_prev, o[q], 0, 0, 0);
+      }
+    }
+    const uint4 xr = e4m3x8_f16(op.rp);
+    const v4f acc_r = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xr), __builtin_bit_cast(v8h, qrope),
+                                                             v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    if (g_new != Gs) {
+      const float f = __builtin_ldexpf(1.0f, max(Gs - g_new, -200));
+#pragma unroll
+      for (int q = 0; q < 16; ++q) o[q] *= f;
+      Gs = g_new;
+    }
+    // this wave's part of the log2-domain scores of keys 4*grp + i, head `row`
+    if (active) {
+      v4f y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[i] = fmaf(c_score * op.s2k[i], acc_l[i], c_rope * acc_r[i]);
+        s2p_prev[i] = __builtin_ldexpf(op.s2k[i], -Gs);   // < 1
+      }
+      xch[(k & 1) * 128 + half * 64 + lane] = y;
+      pair_publish(k + 1);
+    }
+    // ---- next slot's bytes: staged into buffer (k+1)&1 (the PV above was
+    // its last reader); its load buffer is refilled right away
+    stage(raw, pbuf, op);
+    fetch(p + (kBufs + 1) * kPairs, raw);
+  };
+
   const int iters = p_end > p_begin ? (p_end - p_begin + kPairs - 1) / kPairs : 0;
   PageOp op;
   stage(bufs[0], 0, op);   // slot 0 into K-row buffer 0
@@ -465,9 +491,12 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
 #pragma unroll
   for (int j = 0; j < kBufs - 1; ++j)
     if (it + j < iters) step(op, it + j, bufs[(j + 1) % kBufs]);
-  // PV of the last page slot (K-row buffer (iters - 1) & 1; P is zero if
-  // that slot held no page or there was none)
+  // softmax and PV of the last page slot (K-row buffer (iters - 1) & 1; P is
+  // zero if that slot held no page or there was none)
   {
+    pb_prev = v4h{(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
+    const int p_last = p_begin + pair + (iters - 1) * kPairs;
+    if (iters > 0 && p_last < p_end) softmax_of(iters - 1, p_last, s2p_prev);
     const int pbuf = ((iters - 1) & 1) * kKtBytes;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
