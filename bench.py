@@ -348,10 +348,30 @@ def extras(torch, kvq, c, k, v, q, slot, scales):
                               "pct_of_peak": round(100 * cb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
     del cache
     torch.cuda.empty_cache()
+    rows.update(tiny_decode_rows(torch, kvq))
     rows.update(long_context_rows(torch, kvq))
     rows.update(prefill_rows(torch, kvq))
     rows.update(nvfp4_rows(torch, kvq))
     return rows
+
+
+def tiny_decode_rows(torch, kvq):
+    """The tiny decode (2 x 257 tokens, 8/2 heads, head_dim 64, unit scales):
+    a latency row, the 514 tokens stored first."""
+    from workloads import config_tiny_decode
+    c = config_tiny_decode()
+    dev = "cuda"
+    cache = kvq.E4M3Cache(c.num_pages, c.num_kv_heads, c.head_dim)
+    kvq.store(cache, c.k.to(dev), c.v.to(dev), torch.from_numpy(c.slot_mapping).to(dev), 1.0, 1.0)
+    q = c.q.to(dev)
+    bt = torch.from_numpy(c.block_table).to(dev)
+    sl = torch.from_numpy(c.seq_lens).to(dev)
+    out = torch.empty((c.batch, c.num_q_heads, c.head_dim), dtype=torch.bfloat16, device=dev)
+    ms = timed_mean(torch, lambda: kvq.decode(cache, q, bt, sl, c.max_seq_len, c.softmax_scale, 1.0, 1.0, 1.0,
+                                              out=out), reps=20)
+    by = decode_bytes(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim, c.max_seq_len)
+    return {"tiny_decode": {"batch": c.batch, "context": c.max_seq_len, "us": round(ms * 1e3, 2),
+                            "bytes": by}}
 
 
 def nvfp4_rows(torch, kvq):

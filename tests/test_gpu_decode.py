@@ -80,6 +80,16 @@ REL_CASES = [
 ]
 
 
+@pytest.mark.parametrize("splits", [16, 20, 40])
+def test_decode_many_splits(splits):
+    """Split counts at and past the combine's register-prefetch width (16),
+    with sequences short enough that some splits see no key."""
+    c = make_attn_case("many_splits", 300 + splits, [5000, 700, 2049, 17], [1] * 4, 32, 4, 128,
+                       qk_dist="rms20", v_std=4.0, v_outlier_frac=1e-3, slopes=geometric_slopes(32))
+    _, out, ref = run_case(c, num_splits=splits)
+    check_attention(out, ref, "splits=%d" % splits)
+
+
 @pytest.mark.parametrize("lens,hq,hkv,d,window,extent", REL_CASES)
 @pytest.mark.parametrize("splits", [0, 3])
 def test_decode_learned_bias(lens, hq, hkv, d, window, extent, splits):

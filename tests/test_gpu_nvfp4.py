@@ -103,6 +103,15 @@ def test_mla_decode_shapes(std, splits):
     print(check_attention(out, ref, "mla std %g splits %d" % (std, splits)))
 
 
+@pytest.mark.parametrize("splits", [8, 12, 40])
+def test_mla_decode_many_splits(splits):
+    """Split counts at and past the MLA combine's register-prefetch width (8);
+    the 17-key sequence leaves most splits without a key."""
+    c = make_mla_case("mla_splits", 70 + splits, [3000, 1500, 17], layer_std=1.0, rope_scale=1.0)
+    out, ref = run_mla(c, num_splits=splits)
+    check_attention(out, ref, "mla splits %d" % splits)
+
+
 def test_mla_decode_zero_length_and_poison():
     c = make_mla_case("mla0", 61, [0, 33, 5], layer_std=1.0, spare_frac=2.0)
     out, ref = run_mla(c)
