@@ -70,7 +70,7 @@ int check_params(const kvq_cache *c, const kvq_attn_params *p) {
 
 // Split plan for the e4m3 decode kernel. Waves per workgroup and splits are
 // chosen so the grid holds about 8 waves per compute unit, with at least one
-// 128-key block per wave.
+// 128-key block per wave; sequences of up to 8 blocks run as one split.
 kvq::DecodePlan plan_decode(const kvq_cache *c, int32_t num_seqs, int32_t max_seq_len,
                             const kvq_attn_params *p) {
   kvq::DecodePlan pl{};
@@ -85,7 +85,9 @@ kvq::DecodePlan plan_decode(const kvq_cache *c, int32_t num_seqs, int32_t max_se
   const int64_t nblk = pages > 0 ? (pages + 7) / 8 : 1;
   const int64_t units = static_cast<int64_t>(num_seqs) * c->num_kv_heads * pl.qtiles;
   const int64_t target_waves = static_cast<int64_t>(current_cu_count()) * 8;
-  pl.waves = nblk >= 8 ? (c->head_dim == 128 ? 8 : 8) : (nblk >= 4 ? 4 : (nblk >= 2 ? 2 : 1));
+  // the smallest power of two of waves that gives each wave at most one block
+  // of a short sequence (so one split suffices and no combine runs), else 8
+  pl.waves = nblk > 4 ? 8 : (nblk > 2 ? 4 : (nblk > 1 ? 2 : 1));
   int64_t splits;
   if (p->num_splits > 0) {
     splits = p->num_splits;
