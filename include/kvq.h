@@ -103,8 +103,9 @@ typedef struct {
                             window is [PR54705] "Purpose") */
   int32_t num_splits;    /* 0: library's choice; > 0 requests the number of
                             KV splits per (sequence, KV head) in decode. The
-                            library clamps it: at least 4 pages per split,
-                            and for NVFP4 at most 512 pages per split */
+                            library clamps it: e4m3, at least one 128-key
+                            block (8 pages) per split; NVFP4, at least 4 and
+                            at most 512 pages per split */
   int32_t rel_extent;    /* entries per head of rel_bias, 1 .. 1,048,576,
                             when rel_bias is set; 0 otherwise */
   float softmax_scale;   /* finite, > 0 */
