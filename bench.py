@@ -211,6 +211,11 @@ def main():
                    scales["v"], out=out, workspace=ws)
 
     def step(i):
+        # the current tokens' quant-on-store and the decode in one launch
+        kvq.decode(caches[i % 2], q, bt, seq_lens, L, c.softmax_scale, scales["q"], scales["k"],
+                   scales["v"], out=out, workspace=ws, k_new=k_new, v_new=v_new)
+
+    def step_unfused(i):
         kvq.store(caches[i % 2], k_new, v_new, slot_new, scales["k"], scales["v"])
         decode(i)
 
@@ -232,6 +237,8 @@ def main():
     # launch stream, so that no event sits between two launches.
     dec_ms = back_to_back_ms(torch, decode, args.steps)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+    # the same step as two launches (kvq_store, then kvq_paged_attn_decode)
+    unfused_ms = back_to_back_ms(torch, step_unfused, args.steps)
     result = {
         "metric": "fp8 paged-decode attention HBM GB/s & % of peak; KV store tokens/s",
         "value": round(value, 1),
@@ -247,12 +254,14 @@ def main():
         "data": "synthetic (seeded; Q/K RMS-normed amax 20, V std 8 with 0.1% outliers in [448, 1272])",
         "config": {"workload": "batched_decode", "batch": B, "context": L, "q_heads": Hq,
                    "kv_heads": Hkv, "head_dim": D, "page_size": 16, "kv_format": "e4m3",
-                   "scales": scales, "step": "store 64 new tokens + decode attention"},
+                   "scales": scales,
+                   "step": "store 64 new tokens + decode attention, one launch (kvq_paged_attn_decode_append)"},
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "kernel": "decode_e4m3_kernel (batched decode)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_record(),
                      "bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_ms * 1e3, 2)},
+        "step_unfused_us": round(unfused_ms * 1e3, 2),
     }
     log("decode %.2f us, %.0f GB/s (%.1f%% of peak)" % (dec_ms * 1e3, achieved,
                                                          100 * achieved / HBM_PEAK_GBPS))

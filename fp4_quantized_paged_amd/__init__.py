@@ -49,7 +49,7 @@ FLAG_PREFILL_FP8_P = 1
 
 
 _lib = None
-ABI_VERSION = 3   # KVQ_ABI_VERSION of include/kvq.h
+ABI_VERSION = 4   # KVQ_ABI_VERSION of include/kvq.h
 
 _SIGNATURES = {
     "kvq_abi_version": (ctypes.c_int, []),
@@ -74,6 +74,12 @@ _SIGNATURES = {
                                              ctypes.c_int32, ctypes.c_int32,
                                              ctypes.POINTER(AttnParams), ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "kvq_paged_attn_decode_append": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p,
+                                                    ctypes.c_void_p, ctypes.c_void_p,
+                                                    ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                                    ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.POINTER(AttnParams), ctypes.c_void_p,
+                                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "kvq_paged_attn_prefill": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                               ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
@@ -267,10 +273,19 @@ def decode(cache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Te
            v_scale: float = 1.0, window: int = 0, slopes: Optional[torch.Tensor] = None,
            num_splits: int = 0, out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None,
-           rel_bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+           rel_bias: Optional[torch.Tensor] = None, k_new: Optional[torch.Tensor] = None,
+           v_new: Optional[torch.Tensor] = None) -> torch.Tensor:
     """kvq_paged_attn_decode. q bf16 [B, Hq, Dqk] -> out bf16 [B, Hq, Dv].
-    rel_bias: learned relative-bias table, bf16 [Hq, extent]."""
-    _need_cuda(q, block_table, seq_lens, slopes, rel_bias)
+    rel_bias: learned relative-bias table, bf16 [Hq, extent]. k_new, v_new
+    (bf16 [B, Hkv, D], both or neither): the current tokens' K/V, stored at
+    position seq_lens[b] - 1 with k_scale / v_scale in the same launch
+    (kvq_paged_attn_decode_append)."""
+    _need_cuda(q, block_table, seq_lens, slopes, rel_bias, k_new, v_new)
+    append = k_new is not None or v_new is not None
+    if append:
+        assert k_new is not None and v_new is not None
+        for t in (k_new, v_new):
+            assert t.dtype == torch.bfloat16 and t.is_contiguous()
     assert q.dtype == torch.bfloat16 and q.is_contiguous()
     assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
     B, Hq, _ = q.shape
@@ -283,6 +298,13 @@ def decode(cache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Te
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if append:
+        st = lib().kvq_paged_attn_decode_append(ctypes.byref(d), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                                _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
+                                                B, int(max_seq_len), ctypes.byref(p), _ptr(out),
+                                                _ptr(workspace), ws_bytes, _stream())
+        _check(st, "kvq_paged_attn_decode_append")
+        return out
     st = lib().kvq_paged_attn_decode(ctypes.byref(d), _ptr(q), _ptr(block_table),
                                      block_table.stride(0), _ptr(seq_lens), B, int(max_seq_len),
                                      ctypes.byref(p), _ptr(out), _ptr(workspace), ws_bytes,

@@ -143,6 +143,28 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   const size_t g_off = (size_t)g * kv_head_stride;
   const int32_t *bt = a.block_table + (size_t)b * a.bt_stride;
 
+  // Fused append: the current token (position L - 1, in the last block) is
+  // quantized with the store's quantizer and written into its page by the
+  // wave that reads that block, before it loads the block. With several
+  // query tiles each tile's workgroup writes the same bytes.
+  const int blk_last = nblk - 1;
+  const bool appender = a.k_new != nullptr && L > 0 && blk_last >= blk_begin && blk_last < blk_end &&
+                        wave == (blk_last - blk_begin) % W;
+  if (appender && lane < D / 8) {
+    const int pos = L - 1;
+    const size_t base = (size_t)bt[pos >> 4] * page_stride + g_off;
+    const size_t src = ((size_t)b * a.hkv + g) * D + 8 * lane;
+    const uint2 kq = quant8_e4m3(*(const uint4 *)(a.k_new + src), a.k_inv);
+    const uint2 vq = quant8_e4m3(*(const uint4 *)(a.v_new + src), a.v_inv);
+    *(uint2 *)(a.kc_w + base + (size_t)(pos & 15) * D + 8 * lane) = kq;
+    uint8_t *vdst = a.vc_w + base + (pos & 15) + 16 * (8 * lane);   // token-minor: dim d at 16 d
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vdst[16 * i] = (uint8_t)(vq.x >> (8 * i));
+      vdst[16 * (4 + i)] = (uint8_t)(vq.y >> (8 * i));
+    }
+  }
+
   // head_dim 128: lane l holds the physical page of page (l & 7) of the next
   // block, clamped to the sequence's last page.
   int pid_next = 0;
@@ -152,6 +174,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   }
 
   for (int blk = blk_begin + wave; blk < blk_end; blk += W) {
+    if (appender && blk == blk_last) {
+      // the appended bytes are in memory before this block's loads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
     const int pbase = page_lo + blk * 8;
     // Pages this lane touches: K rows come from pages pbase + 2*(row/4) + {0,1},
     // V columns (and this lane's output keys) from pages pbase + 2*grp + {0,1}.

@@ -275,16 +275,23 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t num_seqs, int3
   return plan_mla(num_seqs, max_seq_len, params).workspace;
 }
 
-int kvq_paged_attn_decode(const kvq_cache *cache, const void *q, const int32_t *block_table,
-                          int64_t block_table_stride, const int32_t *seq_lens, int32_t num_seqs,
-                          int32_t max_seq_len, const kvq_attn_params *params, void *out,
-                          void *workspace, size_t workspace_bytes, kvq_stream_t stream) {
+namespace {
+
+// Decode, with the current tokens' K/V stored first when k_new is set.
+int decode_impl(const kvq_cache *cache, const void *q, const void *k_new, const void *v_new,
+                const int32_t *block_table, int64_t block_table_stride, const int32_t *seq_lens,
+                int32_t num_seqs, int32_t max_seq_len, const kvq_attn_params *params, void *out,
+                void *workspace, size_t workspace_bytes, kvq_stream_t stream) {
   int st = check_cache(cache);
   if (st != KVQ_OK) return st;
   st = check_params(cache, params);
   if (st != KVQ_OK) return st;
+  const bool append = k_new != nullptr || v_new != nullptr;
+  if (append && cache->format != KVQ_FMT_E4M3) return KVQ_ERR_UNSUPPORTED;
   if (num_seqs < 0 || max_seq_len < 0) return KVQ_ERR_INVALID_ARG;
   if (num_seqs == 0) return KVQ_OK;
+  if (append && (k_new == nullptr || v_new == nullptr || !aligned16(k_new) || !aligned16(v_new)))
+    return KVQ_ERR_INVALID_ARG;
   if (q == nullptr || block_table == nullptr || seq_lens == nullptr || out == nullptr) return KVQ_ERR_INVALID_ARG;
   if (!aligned16(q)) return KVQ_ERR_INVALID_ARG;
   if (block_table_stride * 16 < max_seq_len) return KVQ_ERR_INVALID_ARG;
@@ -316,6 +323,14 @@ int kvq_paged_attn_decode(const kvq_cache *cache, const void *q, const int32_t *
     a.q_inv = 1.0f / params->q_scale;
     a.fold_log2 = params->softmax_scale * params->q_scale * params->k_scale * 1.4426950408889634f;
     a.v_scale = params->v_scale;
+    if (append) {
+      a.k_new = static_cast<const uint16_t *>(k_new);
+      a.v_new = static_cast<const uint16_t *>(v_new);
+      a.kc_w = static_cast<uint8_t *>(cache->k);
+      a.vc_w = static_cast<uint8_t *>(cache->v);
+      a.k_inv = 1.0f / params->k_scale;   // as kvq_store computes them
+      a.v_inv = 1.0f / params->v_scale;
+    }
     return hip_status(kvq::launch_decode_e4m3(a, pl, reinterpret_cast<hipStream_t>(stream)));
   }
   if (params->num_q_heads != 16) return KVQ_ERR_UNSUPPORTED;
@@ -339,6 +354,27 @@ int kvq_paged_attn_decode(const kvq_cache *cache, const void *q, const int32_t *
   a.scale_log2 = params->softmax_scale * 1.4426950408889634f;
   a.rope_scale = params->k_scale;
   return hip_status(kvq::launch_decode_mla(a, pl, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int kvq_paged_attn_decode(const kvq_cache *cache, const void *q, const int32_t *block_table,
+                          int64_t block_table_stride, const int32_t *seq_lens, int32_t num_seqs,
+                          int32_t max_seq_len, const kvq_attn_params *params, void *out,
+                          void *workspace, size_t workspace_bytes, kvq_stream_t stream) {
+  return decode_impl(cache, q, nullptr, nullptr, block_table, block_table_stride, seq_lens, num_seqs,
+                     max_seq_len, params, out, workspace, workspace_bytes, stream);
+}
+
+int kvq_paged_attn_decode_append(const kvq_cache *cache, const void *q, const void *k_new,
+                                 const void *v_new, const int32_t *block_table,
+                                 int64_t block_table_stride, const int32_t *seq_lens,
+                                 int32_t num_seqs, int32_t max_seq_len,
+                                 const kvq_attn_params *params, void *out, void *workspace,
+                                 size_t workspace_bytes, kvq_stream_t stream) {
+  if (k_new == nullptr || v_new == nullptr) return KVQ_ERR_INVALID_ARG;
+  return decode_impl(cache, q, k_new, v_new, block_table, block_table_stride, seq_lens, num_seqs,
+                     max_seq_len, params, out, workspace, workspace_bytes, stream);
 }
 
 int kvq_paged_attn_prefill(const kvq_cache *cache, const void *q, const int32_t *cu_q_lens, int64_t total_q,

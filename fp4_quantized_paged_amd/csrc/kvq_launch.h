@@ -73,6 +73,11 @@ struct DecodeE4M3Launch {
   float q_inv;                 // fp32(1/q_scale)
   float fold_log2;             // softmax_scale * q_scale * k_scale * log2(e)
   float v_scale;
+  // fused append (nullptr: none): the current token's bf16 K/V [B][Hkv][D],
+  // quantized with k_inv / v_inv and written at position seq_lens[b] - 1
+  const uint16_t *k_new, *v_new;
+  uint8_t *kc_w, *vc_w;        // the same pools as kc / vc, writable
+  float k_inv, v_inv;
 };
 hipError_t launch_decode_e4m3(const DecodeE4M3Launch &a, const DecodePlan &p, hipStream_t s);
 

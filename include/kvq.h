@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 3
+#define KVQ_ABI_VERSION 4
 
 /* A hipStream_t. NULL selects the null stream. */
 typedef struct ihipStream_t *kvq_stream_t;
@@ -269,6 +269,29 @@ int kvq_paged_attn_decode(const kvq_cache *cache, const void *q,
                           const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
                           const kvq_attn_params *params, void *out, void *workspace,
                           size_t workspace_bytes, kvq_stream_t stream);
+
+/*
+ * kvq_paged_attn_decode_append: kvq_store of each sequence's current token
+ * followed by kvq_paged_attn_decode, in one launch ([PR54705] "Purpose":
+ * quant-on-store of K/V, then decode with the descale fold). KVQ_FMT_E4M3
+ * only (KVQ_ERR_UNSUPPORTED otherwise).
+ *
+ * k_new, v_new: device bf16 [num_seqs][num_kv_heads][head_dim], contiguous,
+ * 16-byte aligned: the K/V of the token at position seq_lens[b] - 1. They are
+ * quantized exactly as kvq_store does with params->k_scale / v_scale and
+ * written into the page the block table gives for that position; then the
+ * attention reads them like every other stored token. The stored bytes and
+ * the output equal those of kvq_store (at the same slots) followed by
+ * kvq_paged_attn_decode. Sequences of length 0 store nothing. All other
+ * arguments, the workspace and the errors are those of
+ * kvq_paged_attn_decode (kvq_decode_workspace_bytes applies unchanged).
+ */
+int kvq_paged_attn_decode_append(const kvq_cache *cache, const void *q, const void *k_new,
+                                 const void *v_new, const int32_t *block_table,
+                                 int64_t block_table_stride, const int32_t *seq_lens,
+                                 int32_t num_seqs, int32_t max_seq_len,
+                                 const kvq_attn_params *params, void *out, void *workspace,
+                                 size_t workspace_bytes, kvq_stream_t stream);
 
 /*
  * kvq_paged_attn_prefill: chunked prefill over the e4m3 cache ([PR54705]

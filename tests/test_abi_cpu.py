@@ -147,6 +147,29 @@ def test_decode_validation(lib):
     assert lib.kvq_decode_workspace_bytes(ctypes.byref(d), 2, 1000, ctypes.byref(params(num_splits=1))) == 0
 
 
+def decode_append(lib, desc, p, kn=FAKE, vn=FAKE, B=2, max_len=100, ws=None, ws_bytes=0):
+    return lib.kvq_paged_attn_decode_append(ctypes.byref(desc), FAKE, kn, vn, FAKE, 64, FAKE, B, max_len,
+                                            ctypes.byref(p), FAKE, ws, ws_bytes, None)
+
+
+def test_decode_append_validation(lib):
+    d = e4m3_desc()
+    assert decode_append(lib, d, params(), kn=None) == -1
+    assert decode_append(lib, d, params(), vn=None) == -1
+    assert decode_append(lib, d, params(), kn=FAKE + 2) == -1        # not 16-byte aligned
+    assert decode_append(lib, d, params(), vn=FAKE + 8) == -1
+    for bad in (0.0, -1.0, math.nan, math.inf):
+        assert decode_append(lib, d, params(k_scale=bad)) == -3
+        assert decode_append(lib, d, params(v_scale=bad)) == -3
+    assert decode_append(lib, d, params(), B=0) == 0                 # no sequences: no launch
+    assert decode_append(lib, d, params(num_q_heads=30)) == -1
+    nv = kvq.CacheDesc(2, 16, 1, 576, 64, FAKE, None)
+    assert decode_append(lib, nv, params(num_q_heads=16)) == -2      # e4m3 only
+    p = params(num_splits=4)
+    need = lib.kvq_decode_workspace_bytes(ctypes.byref(d), 2, 1000, ctypes.byref(p))
+    assert decode_append(lib, d, p, max_len=1000, ws=FAKE, ws_bytes=need - 4) == -4
+
+
 def test_nvfp4_decode_validation(lib):
     nv = kvq.CacheDesc(2, 16, 1, 576, 64, FAKE, None)
     assert decode(lib, nv, params(num_q_heads=8)) == -2                 # MLA decode takes 16 heads

@@ -142,3 +142,46 @@ def test_poisoned_pool_never_read():
         out = dc.decode(s, num_splits=splits)
         torch.cuda.synchronize()
         assert torch.all(torch.isfinite(out.float()))
+
+
+APPEND_CASES = [
+    # (seq_lens, Hq, Hkv, D, window, slopes, splits)
+    ([1, 15, 16, 17, 129, 1000], 8, 2, 64, 0, False, 0),
+    ([0, 5, 300, 2049], 32, 4, 128, 0, True, 0),
+    ([3000, 700], 32, 1, 128, 0, True, 3),          # two query tiles write the same token
+    ([5000, 511, 512, 513], 32, 4, 128, 512, False, 0),
+    ([5000, 17], 32, 4, 128, 0, False, 40),
+]
+
+
+@pytest.mark.parametrize("lens,hq,hkv,d,window,bias,splits", APPEND_CASES)
+def test_decode_append_equals_store_then_decode(lens, hq, hkv, d, window, bias, splits):
+    """kvq_paged_attn_decode_append: the cache bytes and the output equal a
+    kvq_store of the current tokens followed by kvq_paged_attn_decode."""
+    slopes = geometric_slopes(hq) if bias else None
+    c = make_attn_case("append", 400 + len(lens) + hq + d, lens, [1] * len(lens), hq, hkv, d,
+                       qk_dist="rms20", v_std=4.0, v_outlier_frac=1e-3, window=window, slopes=slopes)
+    ref = DeviceCase(c)
+    s = ref.calibrate()
+    ref.store_all(s)
+    ref_out = ref.decode(s, num_splits=splits)
+
+    dc = DeviceCase(c)
+    starts = np.concatenate([[0], np.cumsum(c.seq_lens)])
+    last = {int(starts[b + 1] - 1): b for b, L in enumerate(c.seq_lens) if L > 0}
+    older = torch.tensor([t for t in range(int(starts[-1])) if t not in last], dtype=torch.long).cuda()
+    kvq.store(dc.cache, dc.k[older].contiguous(), dc.v[older].contiguous(), dc.slot[older], s["k"], s["v"])
+    k_new = torch.zeros((c.batch, hkv, d), dtype=torch.bfloat16, device="cuda")
+    v_new = torch.zeros_like(k_new)
+    for t, b in last.items():
+        k_new[b] = dc.k[t]
+        v_new[b] = dc.v[t]
+    out = dc.decode(s, num_splits=splits, k_new=k_new, v_new=v_new)
+    torch.cuda.synchronize()
+    assert torch.equal(dc.cache.k, ref.cache.k) and torch.equal(dc.cache.v, ref.cache.v)
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    so = oracle_scales(c)
+    kc, vc = oracle_cache(c, so)
+    want = paged_decode(c.q.float().numpy(), kc, vc, c.block_table, c.seq_lens, c.softmax_scale,
+                        so["q"], so["k"], so["v"], c.window, c.slopes)
+    check_attention(out, want, "append %s" % lens)
