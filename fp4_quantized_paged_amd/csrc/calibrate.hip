@@ -100,14 +100,38 @@ __global__ void scale_rule_kernel(const float *amax, int rule, float *scale) {
 // counts of the stored values at a scale). Each value is decided with the
 // store's own arithmetic: y = fp32(x) * inv; clipped when |y| > 448 (the
 // clamp changes it; NaN compares false); flushed when the bf16 input is
-// nonzero and not NaN and its e4m3 code is +-0. Per-lane counts, one wave
-// and workgroup reduction, two 64-bit atomic adds per workgroup.
+// nonzero and not NaN and its e4m3 code is +-0. Both decisions are monotone
+// in |x|, and non-negative bf16 values order like their bit patterns, so
+// each band is a range of magnitude patterns: clipped (T, 0x7F80] (0x7F80 is
+// inf), flushed [1, F], with T and F found once per thread by bisection on
+// that same arithmetic (the store's multiply and its hardware conversion).
+// Per-lane counts, one wave and workgroup reduction, two 64-bit atomic adds
+// per workgroup.
+__device__ __forceinline__ float bf16_mag(uint32_t m) { return __uint_as_float(m << 16); }
+
 __global__ __launch_bounds__(kAmaxThreads) void band_kernel(BandLaunch a) {
   __shared__ uint32_t red[2][kAmaxWaves];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t cpr = a.row_len >> 3;
   const int64_t nwaves = (int64_t)gridDim.x * kAmaxWaves;
+  // T: the largest magnitude that the clamp leaves alone (0 does, inf does not)
+  uint32_t lo = 0, hi = 0x7F80u;
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (fabsf(bf16_mag(mid) * a.inv) > kE4M3Max) hi = mid; else lo = mid;
+  }
+  const uint32_t clip_span = 0x7F80u - lo;   // clipped: mag - (T + 1) < clip_span
+  const uint32_t clip_lo = lo + 1;
+  // F: the largest magnitude whose e4m3 code is zero (0 is, 448 / inv is not)
+  lo = 0;
+  hi = 0x7F80u;
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) >> 1;
+    const float y = sat448(bf16_mag(mid) * a.inv);
+    if ((cvt4_e4m3(y, 0.0f, 0.0f, 0.0f) & 0x7Fu) != 0) hi = mid; else lo = mid;
+  }
+  const uint32_t flush_hi = lo;              // flushed: mag - 1 < F
   uint32_t n_clip = 0, n_flush = 0;
   int64_t r = ((int64_t)blockIdx.x * kAmaxWaves + wave) * kRowUnroll;
   for (; r < a.rows; r += nwaves * kRowUnroll) {
@@ -128,16 +152,11 @@ __global__ __launch_bounds__(kAmaxThreads) void band_kernel(BandLaunch a) {
 #pragma unroll
       for (int u = 0; u < kRowUnroll; ++u) {
         const uint32_t wd[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-        const uint2 code = quant8_e4m3(x[u], a.inv);
-        const uint32_t cw[2] = {code.x, code.y};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint32_t h = (wd[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-          const uint32_t mag = h & 0x7FFFu;
-          const float y = __uint_as_float(h << 16) * a.inv;
-          n_clip += fabsf(y) > kE4M3Max ? 1u : 0u;
-          const uint32_t cb = (cw[e >> 2] >> (8 * (e & 3))) & 0x7Fu;
-          n_flush += (mag != 0 && mag <= 0x7F80u && cb == 0) ? 1u : 0u;
+          const uint32_t mag = (wd[e >> 1] >> (16 * (e & 1))) & 0x7FFFu;
+          n_clip += (mag - clip_lo < clip_span) ? 1u : 0u;
+          n_flush += (mag - 1u < flush_hi) ? 1u : 0u;
         }
       }
     }

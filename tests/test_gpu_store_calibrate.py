@@ -184,7 +184,7 @@ def test_store_deterministic():
     assert torch.equal(a.cache.k, b.cache.k) and torch.equal(a.cache.v, b.cache.v)
 
 
-@pytest.mark.parametrize("scale", [1.0, 2.0, 3.0, 0.125, 20.0 / 448])
+@pytest.mark.parametrize("scale", [1.0, 2.0, 3.0, 0.125, 20.0 / 448, 0.7, 1e-3, 1e4, 3.3e-38])
 def test_band_counts_all_bf16_patterns(scale):
     """Clip and flush-to-zero counts over every bf16 pattern, bit-exact."""
     x = all_patterns(4, 128).cuda()
