@@ -8,6 +8,7 @@ from oracle.attention import paged_decode
 from workloads import (config_tiny_decode, config_batched_decode, config_long_context,
                        make_attn_case, geometric_slopes)
 from parity import DeviceCase, oracle_scales, oracle_cache, seq_tokens, check_attention
+from oracle.kvcache import new_cache, store_e4m3
 
 pytestmark = pytest.mark.gpu
 
@@ -185,3 +186,40 @@ def test_decode_append_equals_store_then_decode(lens, hq, hkv, d, window, bias, 
     want = paged_decode(c.q.float().numpy(), kc, vc, c.block_table, c.seq_lens, c.softmax_scale,
                         so["q"], so["k"], so["v"], c.window, c.slopes)
     check_attention(out, want, "append %s" % lens)
+
+
+def test_batched_decode_append_full_size_sampled():
+    """The bench step at full size (64 x 8,192 tokens, 32/4 heads): every token
+    but each sequence's current one stored, then kvq_paged_attn_decode_append.
+    The current tokens' bytes equal the oracle's quantization, and sampled
+    sequences' outputs meet the tolerance and equal a plain decode's bits."""
+    c = config_batched_decode()
+    dc = DeviceCase(c)
+    s = dc.calibrate()
+    so = oracle_scales(c)
+    assert s == so
+    last = np.cumsum(c.seq_lens) - 1
+    keep = np.ones(int(c.seq_lens.sum()), dtype=bool)
+    keep[last] = False
+    older = torch.from_numpy(np.nonzero(keep)[0]).cuda()
+    kvq.store(dc.cache, dc.k[older].contiguous(), dc.v[older].contiguous(), dc.slot[older], s["k"], s["v"])
+    idx = torch.from_numpy(last).cuda()
+    out = dc.decode(s, k_new=dc.k[idx].contiguous(), v_new=dc.v[idx].contiguous())
+    torch.cuda.synchronize()
+    # the appended bytes against the oracle's store of the same 64 tokens
+    kc, vc = new_cache(c.num_pages, c.num_kv_heads, c.page_size, c.head_dim)
+    store_e4m3(kc, vc, c.k.float().numpy()[last], c.v.float().numpy()[last], c.slot_mapping[last],
+               so["k"], so["v"])
+    pages, offs = c.slot_mapping[last] // 16, c.slot_mapping[last] % 16
+    gk, gv = dc.cache.k.cpu().numpy(), dc.cache.v.cpu().numpy()
+    for p, o in zip(pages, offs):
+        assert np.array_equal(gk[p, :, o, :], kc[p, :, o, :])
+        assert np.array_equal(gv[p, :, :, o], vc[p, :, :, o])
+    plain = dc.decode(s)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int16), out.view(torch.int16))
+    seqs = [0, 21, 63]
+    kc2, vc2 = oracle_cache(c, so, tokens=seq_tokens(c, seqs))
+    ref = paged_decode(c.q.float().numpy(), kc2, vc2, c.block_table, c.seq_lens, c.softmax_scale,
+                       so["q"], so["k"], so["v"], c.window, c.slopes, seqs=seqs)
+    print(check_attention(out[torch.tensor(seqs)], ref[seqs], "batched_decode append"))
