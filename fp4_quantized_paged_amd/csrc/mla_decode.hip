@@ -38,11 +38,7 @@
 //    two) only when m or Gs moves;
 //  * pairs merge through LDS; with one split the workgroup writes bf16, else
 //    (O, m, l, m + Gs) partials go to the workspace for the split combine.
-//
-// Prefill (the same page: the readers apply the per-token scale in decode and
-// in the multitile prefill): one workgroup per new query row, one split over
-// the row's causal prefix; new row i of a sequence with Lq new tokens and L
-// keys attends keys 0 .. L - Lq + i with exactly decode's arithmetic.
+
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -156,25 +152,11 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   const int half = wave & 1;
   const int row = lane & 15;      // key of the A operand / head of the output
   const int grp = lane >> 4;
-  // Work item. Decode: (sequence b, split), the query is row b. Prefill: the
-  // query row cu_q_lens[b] + i of sequence b with Lq new tokens sits at
-  // position L_b - Lq + i and attends keys 0 .. that position, one split.
-  int b, split, L, qrow;
-  if (a.cu_q_lens != nullptr) {
-    b = blockIdx.x / a.max_q_len;
-    const int i = blockIdx.x - b * a.max_q_len;
-    const int q0 = a.cu_q_lens[b];
-    const int lq = a.cu_q_lens[b + 1] - q0;
-    if (i >= lq) return;   // the whole workgroup: past this sequence's new tokens
-    split = 0;
-    L = max(0, a.seq_lens[b] - lq + i + 1);
-    qrow = q0 + i;
-  } else {
-    b = blockIdx.x / splits;
-    split = blockIdx.x - b * splits;
-    L = a.seq_lens[b];
-    qrow = b;
-  }
+  // work item: (sequence b, split); the query is row b
+  const int b = blockIdx.x / splits;
+  const int split = blockIdx.x - b * splits;
+  const int L = a.seq_lens[b];
+  const int qrow = b;
   const int npages = (L + 15) >> 4;
   const int p_begin = split * pages_per_split;
   const int p_end = min(npages, p_begin + pages_per_split);
@@ -634,15 +616,6 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const floa
 }
 
 }  // namespace
-
-hipError_t launch_prefill_mla(const DecodeMlaLaunch &a, int max_seq_len, hipStream_t s) {
-  if (a.hq != kHeads || a.cu_q_lens == nullptr || a.max_q_len <= 0) return hipErrorInvalidValue;
-  const int pages = (max_seq_len + 15) / 16;
-  if (pages > kMaxSplitPages) return hipErrorNotSupported;
-  hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)((size_t)a.batch * a.max_q_len)), dim3(kThreads), 0, s, a, 1,
-                     pages > 0 ? pages : 1);
-  return hipGetLastError();
-}
 
 hipError_t launch_decode_mla(const DecodeMlaLaunch &a, const MlaPlan &p, hipStream_t s) {
   if (a.hq != kHeads) return hipErrorNotSupported;

@@ -170,8 +170,10 @@ def test_mla_prefill_long_sampled():
 
 
 def test_mla_prefill_one_token_equals_decode():
-    """One new token per sequence is decode: the prefill rows equal the
-    single-split decode output bit for bit (same kernel, same key order)."""
+    """One new token per sequence is decode: the prefill rows match the
+    single-split decode output (same per-key arithmetic; the prefill kernel
+    sums each 576-dim dot product in one pass, the decode in two 256-dim
+    halves plus RoPE, so the bits may differ by rounding) and the oracle."""
     c = make_mla_case("mla_pf1", 74, [1, 16, 17, 300, 2049], layer_std=1.0)
     cache = kvq.Nvfp4Cache(c.num_pages)
     kvq.store(cache, c.kv.cuda(), None, torch.from_numpy(c.slot_mapping).cuda(), c.rope_scale)
@@ -182,7 +184,13 @@ def test_mla_prefill_one_token_equals_decode():
     cu = torch.arange(c.batch + 1, dtype=torch.int32, device="cuda")
     pf = kvq.prefill(cache, q, cu, 1, bt, sl, c.max_seq_len, c.softmax_scale)
     torch.cuda.synchronize()
-    assert torch.equal(dec, pf)
+    d, f = dec.float(), pf.float()
+    assert float((f - d).norm() / d.norm()) < 1e-3
+    assert bool(((f - d).abs() <= 2e-2 * d.abs().clamp(min=1.0)).all())
+    pool = new_pool(c.num_pages)
+    store_records(pool, c.kv.float().numpy(), c.slot_mapping, c.rope_scale)
+    ref = mla_decode(c.q.float().numpy(), pool, c.block_table, c.seq_lens, c.softmax_scale, c.rope_scale)
+    check_attention(pf, ref, "mla prefill, one new token")
 
 
 def test_mla_prefill_full_size_sampled():
