@@ -10,13 +10,15 @@
 //   out = sum_j p_j s2_j Kt_j / sum_j p_j,   Kt_j = e2m1 * e4m3(group scale).
 //
 // Kernel design (gfx950, wave64): one workgroup per 6 consecutive new rows of
-// a sequence (12 waves, three per SIMD), a wave pair per row. The workgroup walks the rows' pages once:
+// a sequence (12 waves, three per SIMD), a wave pair per row. The workgroup
+// walks the rows' pages once:
 //  * each page's record bytes (5,888) are loaded coalesced two pages ahead,
 //    staged in LDS, and dequantized once for all six rows into an fp16 page
-//    image (16 keys x 576 dims, rows padded to 1,168 bytes so both the
-//    row-slice reads of QK^T and the transposed reads of PV are
-//    conflict-free): the latent as e2m1 * group scale (exact in fp16), the
-//    RoPE part as its e4m3 value; keys past the sequence end become zeros;
+//    image (16 keys x 576 dims, rows padded to 1,168 bytes: the row-slice
+//    reads of QK^T are conflict-free, the transposed reads of PV overlap on
+//    a few banks across two lane groups): the latent as e2m1 * group scale
+//    (exact in fp16), the RoPE part as its e4m3 value; keys past the
+//    sequence end become zeros;
 //  * the two waves of a pair split the dims as the decode does (256 latent +
 //    32 RoPE each for QK^T, v_mfma_f32_16x16x32_f16 with A from the image and
 //    B = fp16 Q*2^k in registers; 256 latent dims each for PV,
