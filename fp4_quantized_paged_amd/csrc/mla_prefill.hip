@@ -14,11 +14,10 @@
 // walks the rows' pages once:
 //  * each page's record bytes (5,888) are loaded coalesced two pages ahead,
 //    staged in LDS, and dequantized once for all six rows into an fp16 page
-//    image (16 keys x 576 dims, rows padded to 1,168 bytes: the row-slice
-//    reads of QK^T are conflict-free, the transposed reads of PV overlap on
-//    a few banks across two lane groups): the latent as e2m1 * group scale
-//    (exact in fp16), the RoPE part as its e4m3 value; keys past the
-//    sequence end become zeros;
+//    image (16 keys x 576 dims, rows placed so that both the row-slice reads
+//    of QK^T and the transposed reads of PV are bank-conflict-free): the
+//    latent as e2m1 * group scale (exact in fp16), the RoPE part as its e4m3
+//    value; keys past the sequence end become zeros;
 //  * the two waves of a pair split the dims as the decode does (256 latent +
 //    32 RoPE each for QK^T, v_mfma_f32_16x16x32_f16 with A from the image and
 //    B = fp16 Q*2^k in registers; 256 latent dims each for PV,
@@ -46,8 +45,13 @@ constexpr int kRec = 368;
 constexpr int kLat = 512;
 constexpr int kDqk = 576;
 constexpr int kHeads = 16;
-constexpr int kImgRow = 2 * kDqk + 16;     // fp16 key row + pad
-constexpr int kImgBytes = 16 * kImgRow;
+// Page image rows: key r's 576 fp16 at byte 1,184 r + 16 (r >> 3). The row
+// stride is 296 dwords (an odd multiple of 8 banks) and keys 8..15 sit 4 banks
+// further, so a QK^T row-slice read (16 keys x 4 dwords) and a transposed PV
+// read (8 keys x 8 dwords per pass) each cover the 64 banks once.
+constexpr int kImgRow = 2 * kDqk + 32;
+constexpr int kImgBytes = 16 * kImgRow + 16;
+__device__ __forceinline__ int img_row(int r) { return r * kImgRow + 16 * (r >> 3); }
 constexpr int kPageBytes = 16 * kRec;
 constexpr int kRawChunks = kPageBytes / 16;            // 368 16-byte chunks per page
 constexpr int kImgChunks = 16 * (kDqk / 8);            // 1,152 fp16 chunks of 8 per page
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void mla_prefill_kernel(DecodeMlaLaunch a
                          h2_bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true)));
         }
       }
-      *(uint4 *)(img + r * kImgRow + 16 * j) = x;
+      *(uint4 *)(img + img_row(r) + 16 * j) = x;
     }
     if (tid < 16) sm.s2[buf][tid] = p * 16 + tid < L ? *(const float *)(raw + tid * kRec + 292) : 0.0f;
   };
@@ -196,9 +200,9 @@ __global__ __launch_bounds__(kThreads) void mla_prefill_kernel(DecodeMlaLaunch a
   // QK^T A operand: key `row`, latent dims 256*half + 32c + 8*grp, RoPE dims
   // 512 + 32*half + 8*grp; PV A operand (transposed): lane s of group grp
   // reads key 4*grp + s/4, dims 256*half + 16q + 4(s%4)
-  const int a_off = row * kImgRow + 512 * half + 16 * grp;
-  const int r_off = row * kImgRow + 2 * kLat + 64 * half + 16 * grp;
-  const int t_off = (4 * grp + (row >> 2)) * kImgRow + 2 * (256 * half + 4 * (row & 3));
+  const int a_off = img_row(row) + 512 * half + 16 * grp;
+  const int r_off = img_row(row) + 2 * kLat + 64 * half + 16 * grp;
+  const int t_off = img_row(4 * grp + (row >> 2)) + 2 * (256 * half + 4 * (row & 3));
 
   for (int k = 0; k < npages; ++k) {
     const int cur = k % 3;
