@@ -136,6 +136,41 @@ def _need_cuda(*ts):
             raise ValueError("kvq needs device tensors")
 
 
+def _check_rows(name: str, t: torch.Tensor, inner: tuple) -> None:
+    """t is bf16 [T, *inner] with the inner dims dense (token stride free)."""
+    if t.dtype != torch.bfloat16 or tuple(t.shape[1:]) != tuple(inner):
+        raise ValueError("%s must be bf16 [T, %s], got %s %s" % (name, ", ".join(map(str, inner)),
+                                                                 t.dtype, tuple(t.shape)))
+    step = 1
+    for dim in range(t.dim() - 1, 0, -1):
+        if t.shape[dim] > 1 and t.stride(dim) != step:
+            raise ValueError("%s: each token's %s elements must be contiguous (strides %s)"
+                             % (name, "x".join(map(str, inner)), tuple(t.stride())))
+        step *= t.shape[dim]
+
+
+def _head_dims(cache) -> tuple:
+    d = cache.desc
+    return (576, 512) if d.format == FMT_NVFP4_MLA368 else (d.head_dim, d.head_dim)
+
+
+def _check_decode_args(cache, q, block_table, seq_lens) -> None:
+    dqk, _ = _head_dims(cache)
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous() or q.shape[2] != dqk:
+        raise ValueError("q must be contiguous bf16 [B, Hq, %d], got %s %s" % (dqk, q.dtype, tuple(q.shape)))
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be int32 [B, pages] with unit inner stride")
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 vector")
+    if seq_lens.shape[0] != q.shape[0] or block_table.shape[0] < q.shape[0]:
+        raise ValueError("q, seq_lens and block_table disagree on the number of sequences")
+
+
+def _check_out(out: torch.Tensor, shape: tuple) -> None:
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(shape) or not out.is_contiguous():
+        raise ValueError("out must be contiguous bf16 %s, got %s %s" % (shape, out.dtype, tuple(out.shape)))
+
+
 class E4M3Cache:
     """Paged e4m3 K/V pools: K u8 [pages][Hkv][16][D], V u8 [pages][Hkv][D][16]."""
 
@@ -172,9 +207,19 @@ def store(cache, k: torch.Tensor, v: Optional[torch.Tensor], slot_mapping: torch
     """kvq_store. E4M3: k, v bf16 [T, Hkv, D]; NVFP4: k bf16 [T, 576], v None
     and k_scale the RoPE scale. slot_mapping int64 [T] (negative: skip)."""
     _need_cuda(k, v, slot_mapping)
-    assert slot_mapping.dtype == torch.int64 and k.dtype == torch.bfloat16
     d = cache.desc
     T = k.shape[0]
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,) or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int64 [T] vector")
+    if d.format == FMT_NVFP4_MLA368:
+        _check_rows("k", k, (576,))
+        if v is not None:
+            raise ValueError("the NVFP4 record store takes no v")
+    else:
+        _check_rows("k", k, (d.num_kv_heads, d.head_dim))
+        if v is None or v.shape[0] != T:
+            raise ValueError("v must hold the same tokens as k")
+        _check_rows("v", v, (d.num_kv_heads, d.head_dim))
     st = lib().kvq_store(ctypes.byref(d), _ptr(k), k.stride(0), _ptr(v),
                          v.stride(0) if v is not None else 0, _ptr(slot_mapping), T,
                          float(k_scale), float(v_scale), _stream())
@@ -186,7 +231,9 @@ def store_nvfp4_static(cache, x: torch.Tensor, slot_mapping: torch.Tensor, rope_
     """kvq_store_nvfp4_static: NVFP4 records with one static outer scale for
     every token. x bf16 [T, 576], slot_mapping int64 [T]."""
     _need_cuda(x, slot_mapping)
-    assert slot_mapping.dtype == torch.int64 and x.dtype == torch.bfloat16
+    _check_rows("x", x, (576,))
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (x.shape[0],) or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int64 [T] vector")
     st = lib().kvq_store_nvfp4_static(ctypes.byref(cache.desc), _ptr(x), x.stride(0), _ptr(slot_mapping),
                                       x.shape[0], float(rope_scale), float(outer_scale), _stream())
     _check(st, "kvq_store_nvfp4_static")
@@ -284,15 +331,19 @@ def decode(cache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Te
     append = k_new is not None or v_new is not None
     if append:
         assert k_new is not None and v_new is not None
+        d0 = cache.desc
         for t in (k_new, v_new):
-            assert t.dtype == torch.bfloat16 and t.is_contiguous()
-    assert q.dtype == torch.bfloat16 and q.is_contiguous()
-    assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+            if (t.dtype != torch.bfloat16 or not t.is_contiguous()
+                    or tuple(t.shape) != (q.shape[0], d0.num_kv_heads, d0.head_dim)):
+                raise ValueError("k_new / v_new must be contiguous bf16 [B, Hkv, D]")
+    _need_cuda(out)
+    _check_decode_args(cache, q, block_table, seq_lens)
     B, Hq, _ = q.shape
     d = cache.desc
-    dv = 512 if d.format == FMT_NVFP4_MLA368 else d.head_dim
+    dv = _head_dims(cache)[1]
     if out is None:
         out = torch.empty((B, Hq, dv), dtype=torch.bfloat16, device=q.device)
+    _check_out(out, (B, Hq, dv))
     p = _params(Hq, softmax_scale, q_scale, k_scale, v_scale, window, slopes, num_splits, rel_bias)
     need = int(lib().kvq_decode_workspace_bytes(ctypes.byref(d), B, int(max_seq_len), ctypes.byref(p)))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
@@ -322,13 +373,22 @@ def prefill(cache, q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,
     """kvq_paged_attn_prefill. q bf16 [sumQ, Hq, Dqk] -> out bf16 [sumQ, Hq, Dv].
     rel_bias: learned relative-bias table, bf16 [Hq, extent]. fp8_p: the
     single-term e4m3 P speed variant (KVQ_FLAG_PREFILL_FP8_P)."""
-    _need_cuda(q, cu_q_lens, block_table, seq_lens, slopes, rel_bias)
-    assert q.dtype == torch.bfloat16 and q.is_contiguous()
+    _need_cuda(q, cu_q_lens, block_table, seq_lens, slopes, rel_bias, out)
+    dqk, dv = _head_dims(cache)
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous() or q.shape[2] != dqk:
+        raise ValueError("q must be contiguous bf16 [sumQ, Hq, %d], got %s %s" % (dqk, q.dtype, tuple(q.shape)))
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be int32 [B, pages] with unit inner stride")
+    B = int(seq_lens.shape[0])
+    if (seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or not seq_lens.is_contiguous()
+            or cu_q_lens.dtype != torch.int32 or tuple(cu_q_lens.shape) != (B + 1,)
+            or not cu_q_lens.is_contiguous() or block_table.shape[0] < B):
+        raise ValueError("seq_lens int32 [B], cu_q_lens int32 [B + 1] and block_table [>= B, pages] expected")
     total_q, Hq, D = q.shape
     d = cache.desc
-    dv = 512 if d.format == FMT_NVFP4_MLA368 else D
     if out is None:
         out = torch.empty((total_q, Hq, dv), dtype=torch.bfloat16, device=q.device)
+    _check_out(out, (total_q, Hq, dv))
     p = _params(Hq, softmax_scale, q_scale, k_scale, v_scale, window, slopes, 0, rel_bias,
                 FLAG_PREFILL_FP8_P if fp8_p else 0)
     st = lib().kvq_paged_attn_prefill(ctypes.byref(d), _ptr(q), _ptr(cu_q_lens), total_q,

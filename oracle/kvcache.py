@@ -94,8 +94,3 @@ def calibrate_amax(x: np.ndarray, slot_mapping=None, prev_amax: float = 0.0):
         amax = np.maximum(amax, np.max(np.abs(rows)))
     scale = np.float32(amax) / np.float32(E4M3_MAX)
     return np.float32(amax), np.float32(scale)
-
-
-def dequantize_e4m3(codes: np.ndarray, scale: float) -> np.ndarray:
-    """codes -> float64 values times the per-tensor scale."""
-    return e4m3_decode(codes) * float(scale)
