@@ -22,7 +22,10 @@ PAGE_SIZE = 16
 RECORD_BYTES = 368
 
 STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
-          -3: "KVQ_ERR_BAD_SCALE", -4: "KVQ_ERR_WORKSPACE", -5: "KVQ_ERR_HIP"}
+          -3: "KVQ_ERR_BAD_SCALE", -4: "KVQ_ERR_WORKSPACE", -5: "KVQ_ERR_HIP",
+          -6: "KVQ_ERR_SCRATCH_LIMIT"}
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # KVQ_NOALLOC_SCRATCH_BYTES of include/kvq.h
 
 
 class KvqError(RuntimeError):
@@ -49,7 +52,7 @@ FLAG_PREFILL_FP8_P = 1
 
 
 _lib = None
-ABI_VERSION = 4   # KVQ_ABI_VERSION of include/kvq.h
+ABI_VERSION = 5   # KVQ_ABI_VERSION of include/kvq.h
 
 _SIGNATURES = {
     "kvq_abi_version": (ctypes.c_int, []),
@@ -80,6 +83,11 @@ _SIGNATURES = {
                                                     ctypes.c_int32, ctypes.c_int32,
                                                     ctypes.POINTER(AttnParams), ctypes.c_void_p,
                                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "kvq_paged_attn_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p,
+                                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                                     ctypes.c_int32, ctypes.c_int32,
+                                                     ctypes.POINTER(AttnParams), ctypes.c_void_p,
+                                                     ctypes.c_void_p]),
     "kvq_paged_attn_prefill": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                               ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
@@ -361,6 +369,30 @@ def decode(cache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Te
                                      ctypes.byref(p), _ptr(out), _ptr(workspace), ws_bytes,
                                      _stream())
     _check(st, "kvq_paged_attn_decode")
+    return out
+
+
+def decode_noalloc(cache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                   max_seq_len: int, softmax_scale: float, q_scale: float = 1.0, k_scale: float = 1.0,
+                   v_scale: float = 1.0, window: int = 0, slopes: Optional[torch.Tensor] = None,
+                   num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                   rel_bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """kvq_paged_attn_decode_noalloc: decode with the split partials in the
+    library's static scratch array (no workspace). Pass ``out`` to keep the
+    call free of allocations on this side too."""
+    _need_cuda(q, block_table, seq_lens, slopes, rel_bias, out)
+    _check_decode_args(cache, q, block_table, seq_lens)
+    B, Hq, _ = q.shape
+    d = cache.desc
+    dv = 512 if d.format == FMT_NVFP4_MLA368 else d.head_dim
+    if out is None:
+        out = torch.empty((B, Hq, dv), dtype=torch.bfloat16, device=q.device)
+    _check_out(out, (B, Hq, dv))
+    p = _params(Hq, softmax_scale, q_scale, k_scale, v_scale, window, slopes, num_splits, rel_bias)
+    st = lib().kvq_paged_attn_decode_noalloc(ctypes.byref(d), _ptr(q), _ptr(block_table),
+                                             block_table.stride(0), _ptr(seq_lens), B, int(max_seq_len),
+                                             ctypes.byref(p), _ptr(out), _stream())
+    _check(st, "kvq_paged_attn_decode_noalloc")
     return out
 
 

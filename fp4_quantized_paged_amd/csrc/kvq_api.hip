@@ -152,6 +152,7 @@ const char *kvq_status_str(int status) {
     case KVQ_ERR_BAD_SCALE: return "scale is not finite and positive";
     case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
     case KVQ_ERR_HIP: return "HIP runtime error";
+    case KVQ_ERR_SCRATCH_LIMIT: return "split partials exceed the static scratch array (KVQ_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -275,13 +276,15 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t num_seqs, int3
   return plan_mla(num_seqs, max_seq_len, params).workspace;
 }
 
-namespace {
+}  // extern "C"
 
-// Decode, with the current tokens' K/V stored first when k_new is set.
-int decode_impl(const kvq_cache *cache, const void *q, const void *k_new, const void *v_new,
-                const int32_t *block_table, int64_t block_table_stride, const int32_t *seq_lens,
-                int32_t num_seqs, int32_t max_seq_len, const kvq_attn_params *params, void *out,
-                void *workspace, size_t workspace_bytes, kvq_stream_t stream) {
+namespace kvq {
+
+int decode_check(const kvq_cache *cache, const void *q, const void *k_new, const void *v_new,
+                 const int32_t *block_table, int64_t block_table_stride, const int32_t *seq_lens,
+                 int32_t num_seqs, int32_t max_seq_len, const kvq_attn_params *params, void *out,
+                 size_t *workspace_needed) {
+  *workspace_needed = 0;
   int st = check_cache(cache);
   if (st != KVQ_OK) return st;
   st = check_params(cache, params);
@@ -296,9 +299,28 @@ int decode_impl(const kvq_cache *cache, const void *q, const void *k_new, const 
   if (!aligned16(q)) return KVQ_ERR_INVALID_ARG;
   if (block_table_stride * 16 < max_seq_len) return KVQ_ERR_INVALID_ARG;
   if (cache->format == KVQ_FMT_E4M3) {
+    *workspace_needed = plan_decode(cache, num_seqs, max_seq_len, params).workspace;
+    return KVQ_OK;
+  }
+  if (params->num_q_heads != 16) return KVQ_ERR_UNSUPPORTED;
+  if (max_seq_len > kMlaMaxSeqLen) return KVQ_ERR_UNSUPPORTED;
+  *workspace_needed = plan_mla(num_seqs, max_seq_len, params).workspace;
+  return KVQ_OK;
+}
+
+int decode_run(const kvq_cache *cache, const void *q, const void *k_new, const void *v_new,
+               const int32_t *block_table, int64_t block_table_stride, const int32_t *seq_lens,
+               int32_t num_seqs, int32_t max_seq_len, const kvq_attn_params *params, void *out,
+               void *workspace, size_t workspace_bytes, kvq_stream_t stream) {
+  size_t need = 0;
+  int st = decode_check(cache, q, k_new, v_new, block_table, block_table_stride, seq_lens, num_seqs,
+                        max_seq_len, params, out, &need);
+  if (st != KVQ_OK || num_seqs == 0) return st;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return KVQ_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return KVQ_ERR_INVALID_ARG;
+  const bool append = k_new != nullptr || v_new != nullptr;
+  if (cache->format == KVQ_FMT_E4M3) {
     const kvq::DecodePlan pl = plan_decode(cache, num_seqs, max_seq_len, params);
-    if (pl.workspace > 0 && (workspace == nullptr || workspace_bytes < pl.workspace)) return KVQ_ERR_WORKSPACE;
-    if (pl.workspace > 0 && !aligned16(workspace)) return KVQ_ERR_INVALID_ARG;
     kvq::DecodeE4M3Launch a{};
     a.q = static_cast<const uint16_t *>(q);
     a.kc = static_cast<const uint8_t *>(cache->k);
@@ -333,11 +355,7 @@ int decode_impl(const kvq_cache *cache, const void *q, const void *k_new, const 
     }
     return hip_status(kvq::launch_decode_e4m3(a, pl, reinterpret_cast<hipStream_t>(stream)));
   }
-  if (params->num_q_heads != 16) return KVQ_ERR_UNSUPPORTED;
-  if (max_seq_len > kMlaMaxSeqLen) return KVQ_ERR_UNSUPPORTED;
   const kvq::MlaPlan pl = plan_mla(num_seqs, max_seq_len, params);
-  if (pl.workspace > 0 && (workspace == nullptr || workspace_bytes < pl.workspace)) return KVQ_ERR_WORKSPACE;
-  if (pl.workspace > 0 && !aligned16(workspace)) return KVQ_ERR_INVALID_ARG;
   kvq::DecodeMlaLaunch a{};
   a.q = static_cast<const uint16_t *>(q);
   a.records = static_cast<const uint8_t *>(cache->k);
@@ -356,13 +374,15 @@ int decode_impl(const kvq_cache *cache, const void *q, const void *k_new, const 
   return hip_status(kvq::launch_decode_mla(a, pl, reinterpret_cast<hipStream_t>(stream)));
 }
 
-}  // namespace
+}  // namespace kvq
+
+extern "C" {
 
 int kvq_paged_attn_decode(const kvq_cache *cache, const void *q, const int32_t *block_table,
                           int64_t block_table_stride, const int32_t *seq_lens, int32_t num_seqs,
                           int32_t max_seq_len, const kvq_attn_params *params, void *out,
                           void *workspace, size_t workspace_bytes, kvq_stream_t stream) {
-  return decode_impl(cache, q, nullptr, nullptr, block_table, block_table_stride, seq_lens, num_seqs,
+  return kvq::decode_run(cache, q, nullptr, nullptr, block_table, block_table_stride, seq_lens, num_seqs,
                      max_seq_len, params, out, workspace, workspace_bytes, stream);
 }
 
@@ -373,7 +393,7 @@ int kvq_paged_attn_decode_append(const kvq_cache *cache, const void *q, const vo
                                  const kvq_attn_params *params, void *out, void *workspace,
                                  size_t workspace_bytes, kvq_stream_t stream) {
   if (k_new == nullptr || v_new == nullptr) return KVQ_ERR_INVALID_ARG;
-  return decode_impl(cache, q, k_new, v_new, block_table, block_table_stride, seq_lens, num_seqs,
+  return kvq::decode_run(cache, q, k_new, v_new, block_table, block_table_stride, seq_lens, num_seqs,
                      max_seq_len, params, out, workspace, workspace_bytes, stream);
 }
 

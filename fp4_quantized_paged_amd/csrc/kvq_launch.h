@@ -1,9 +1,11 @@
-// Internal launch interface between the C-ABI layer (kvq_api.cpp) and the
+// Internal launch interface between the C-ABI layer (kvq_api.hip) and the
 // kernel translation units. Host code only; not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "../../include/kvq.h"
 
 namespace kvq {
 
@@ -122,5 +124,19 @@ struct MlaPlan {
   size_t workspace;
 };
 hipError_t launch_decode_mla(const DecodeMlaLaunch &a, const MlaPlan &p, hipStream_t s);
+
+// Decode entry shared by the public decode calls (kvq_api.hip). decode_check
+// runs every host-side check of the arguments except the workspace and sets
+// the workspace bytes the call needs (0 when num_seqs is 0 or one split
+// suffices); decode_run checks again, checks the workspace and launches.
+// k_new / v_new non-null: the fused append.
+int decode_check(const kvq_cache *cache, const void *q, const void *k_new, const void *v_new,
+                 const int32_t *block_table, int64_t block_table_stride, const int32_t *seq_lens,
+                 int32_t num_seqs, int32_t max_seq_len, const kvq_attn_params *params, void *out,
+                 size_t *workspace_needed);
+int decode_run(const kvq_cache *cache, const void *q, const void *k_new, const void *v_new,
+               const int32_t *block_table, int64_t block_table_stride, const int32_t *seq_lens,
+               int32_t num_seqs, int32_t max_seq_len, const kvq_attn_params *params, void *out,
+               void *workspace, size_t workspace_bytes, kvq_stream_t stream);
 
 }  // namespace kvq

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 4
+#define KVQ_ABI_VERSION 5
 
 /* A hipStream_t. NULL selects the null stream. */
 typedef struct ihipStream_t *kvq_stream_t;
@@ -51,7 +51,10 @@ typedef enum {
   KVQ_ERR_BAD_SCALE = -3,   /* a scale that is not finite and > 0,
                                [PR54705] "Purpose", unity-scale bullet */
   KVQ_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required */
-  KVQ_ERR_HIP = -5          /* a HIP runtime call or launch failed */
+  KVQ_ERR_HIP = -5,         /* a HIP runtime call or launch failed */
+  KVQ_ERR_SCRATCH_LIMIT = -6 /* kvq_paged_attn_decode_noalloc: the call's split
+                               partials exceed the library's static scratch
+                               array (KVQ_NOALLOC_SCRATCH_BYTES) */
 } kvq_status;
 
 typedef enum {
@@ -292,6 +295,34 @@ int kvq_paged_attn_decode_append(const kvq_cache *cache, const void *q, const vo
                                  int32_t num_seqs, int32_t max_seq_len,
                                  const kvq_attn_params *params, void *out, void *workspace,
                                  size_t workspace_bytes, kvq_stream_t stream);
+
+/*
+ * kvq_paged_attn_decode_noalloc: kvq_paged_attn_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). It takes no workspace: the split
+ * partials go to a static device array of the library,
+ * KVQ_NOALLOC_SCRATCH_BYTES per device, which each device holds from this
+ * entry point's first call on it until the process ends. The call allocates
+ * nothing; its first call on a device looks up that device's copy of the
+ * array (hipGetSymbolAddress), with that device current.
+ *
+ * Arguments, arithmetic, output and errors are those of kvq_paged_attn_decode
+ * (same kernels, same split plan: the output is bit-identical), plus
+ * KVQ_ERR_SCRATCH_LIMIT, returned before anything is launched, when
+ * kvq_decode_workspace_bytes(...) for these arguments exceeds
+ * KVQ_NOALLOC_SCRATCH_BYTES (lower num_splits, or use kvq_paged_attn_decode
+ * with a workspace). Every call on one device shares its array and leaves the
+ * last call's partials in it (nothing there needs to start at zero: each
+ * partial is written before it is read within the call): two calls that
+ * overlap in time on one device (different streams, no ordering between
+ * them) race and may return wrong outputs. Calls ordered on one stream are
+ * safe.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int kvq_paged_attn_decode_noalloc(const kvq_cache *cache, const void *q,
+                                  const int32_t *block_table, int64_t block_table_stride,
+                                  const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                  const kvq_attn_params *params, void *out, kvq_stream_t stream);
 
 /*
  * kvq_paged_attn_prefill: chunked prefill over the e4m3 cache ([PR54705]

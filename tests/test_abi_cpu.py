@@ -36,8 +36,9 @@ def test_exports_every_declared_symbol(lib):
     hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kvq.h")).read()
     version = int(re.search(r"#define KVQ_ABI_VERSION (\d+)", hdr).group(1))
     assert lib.kvq_abi_version() == version == kvq.ABI_VERSION
-    for s in (0, -1, -2, -3, -4, -5):
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert lib.kvq_status_str(s)
+    assert lib.kvq_status_str(-6) != lib.kvq_status_str(-99)
 
 
 def e4m3_desc(**kw):
@@ -168,6 +169,29 @@ def test_decode_append_validation(lib):
     p = params(num_splits=4)
     need = lib.kvq_decode_workspace_bytes(ctypes.byref(d), 2, 1000, ctypes.byref(p))
     assert decode_append(lib, d, p, max_len=1000, ws=FAKE, ws_bytes=need - 4) == -4
+
+
+def test_decode_noalloc_validation(lib):
+    """The no-alloc decode runs decode's host checks, then refuses a plan whose
+    partials exceed the static scratch array; neither path launches."""
+    f = lib.kvq_paged_attn_decode_noalloc
+    d = e4m3_desc(num_pages=64 * 256)
+
+    def call(p, B=2, max_len=100):
+        return f(ctypes.byref(d), FAKE, FAKE, 256, FAKE, B, max_len, ctypes.byref(p), FAKE, None)
+
+    assert call(params(num_q_heads=30)) == -1
+    assert call(params(q_scale=0.0)) == -3
+    assert call(params(), B=0) == 0
+    assert call(params(), max_len=256 * 16 + 1) == -1          # table too short
+    assert f(ctypes.byref(d), FAKE + 2, FAKE, 256, FAKE, 2, 100, ctypes.byref(params()), FAKE, None) == -1
+    p = params(num_splits=32)
+    need = lib.kvq_decode_workspace_bytes(ctypes.byref(d), 64, 4096, ctypes.byref(p))
+    assert need == 64 * 32 * 32 * (128 + 2) * 4 > kvq.NOALLOC_SCRATCH_BYTES
+    assert call(p, B=64, max_len=4096) == -6
+    nv = kvq.CacheDesc(2, 16, 1, 576, 64, FAKE, None)
+    assert f(ctypes.byref(nv), FAKE, FAKE, 64, FAKE, 2, 100, ctypes.byref(params(num_q_heads=8)), FAKE,
+             None) == -2
 
 
 def test_nvfp4_decode_validation(lib):
