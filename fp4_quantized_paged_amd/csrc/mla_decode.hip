@@ -28,7 +28,10 @@
 //    row segments into one dim x 4 keys operand. The PV of page k-1 is
 //    interleaved with the dequant and QK^T of page k, so the vector ALU and
 //    the matrix cores work at the same time;
-//  * each wave keeps four pages of record bytes in flight;
+//  * each wave keeps four pages of record bytes in flight, loaded straight
+//    into the MFMA operand layout (lane = key, 32 contiguous nibble bytes of
+//    its dim slice, the four group scales, eight RoPE codes, and the outer
+//    scales of the four keys whose scores the lane holds);
 //  * P enters PV in fp16. Per pair, Gs is the largest exponent of the outer
 //    scales seen so far; the keys' scales enter P as s2 * 2^-Gs < 1. Per head,
 //    the running max m is integer-valued and raised only when a score passes
@@ -114,36 +117,26 @@ __device__ __forceinline__ uint32_t bf16x2_absmax(uint32_t w) {
 
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
 
-// One wave's share of a page's record bytes, as loaded (coalesced: lane l
-// holds 16 bytes; see fetch): latent nibbles of the wave's 256 dims, then
-// four 16-byte chunks per key: group scales, the chunk holding s2, and the
-// wave's 32 RoPE codes.
-struct PageRaw {
-  v4u nib[2];
-  v4u tail;
-};
-
-// the same bytes in the MFMA layout (lane = key `row`, dim group `grp`)
+// One wave's share of a page's record bytes, loaded in the MFMA layout
+// (lane = key `row`, dim group `grp`).
 struct PageOp {
   v4u nib[2];      // e2m1 codes of dims 64*grp .. +64 of the wave's 256
   uint32_t sc;     // their four group scales
   uint2 rp;        // RoPE codes of dims 32*half + 8*grp .. +8
-  float s2;        // the key's outer scale
   float s2k[4];    // outer scales of keys 4*grp + i (this lane's scores)
 };
 
-// LDS staging of one wave's page bytes inside its current K-row buffer
-// (read back before the dequant overwrites it): nibbles of key r at 144*r
-// (128 bytes + pad), chunks of key r at kStageTail + 80*r (64 bytes + pad)
-constexpr int kStageNib = 144;
-constexpr int kStageTail = 16 * kStageNib;
-constexpr int kStageTailRow = 80;
+// Spins of a pair wait before the wave gives up (each spin sleeps ~64
+// cycles; a normal wait takes a few spins). A wave that gives up marks the
+// workgroup and its outputs become NaN instead of the kernel hanging.
+constexpr int kSpinLimit = 1 << 22;
 
 __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a, int splits, int pages_per_split) {
   __shared__ __align__(16) uint8_t smem[kSmemBytes];
   __shared__ float s_m[kPairs][kHeads], s_l[kPairs][kHeads], s_e[kPairs][kHeads];
   __shared__ int s_k[kHeads];
   __shared__ int s_flag[kPairs][2];                    // pages whose half scores are published
+  __shared__ int s_err;                                // a pair wait gave up
   __shared__ int s_bt[kMaxSplitPages];                 // this split's block-table slice
 
   const int lane = threadIdx.x & 63;
@@ -172,24 +165,29 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     btt[j] = bt[p_begin + max(0, min((int)threadIdx.x + j * kThreads, nbt - 1))];
   __builtin_amdgcn_sched_barrier(0);
 
-  // coalesced page loads: nibble load i, lane l -> key 8i + l/8, bytes
-  // 128*half + 16*(l%8); chunk load, lane l -> key l/4, chunk l%4 of
-  // {scales 256 + 16*half, s2 block 288, RoPE 304 + 32*half, +16}
-  const uint32_t off_nib = (lane >> 3) * kRec + 128 * half + 16 * (lane & 7);
-  const int tch = lane & 3;
-  const uint32_t off_tail = (lane >> 2) * kRec + (tch == 0 ? 256 + 16 * half : (tch == 1 ? 288 : 304 + 32 * half + 16 * (tch - 2)));
-  // Every page slot issues the same five loads, so the wait for one buffer
-  // never covers the later buffers' loads in flight. Without a page to fetch
-  // they read this sequence's Q block instead (18 KB, read anyway, unused).
+  // Operand loads, per lane: key `row` of the page at byte 368*row; the
+  // nibbles of dims 256*half + 64*grp .. +64 (32 bytes), their group scales
+  // (4 bytes), the RoPE codes of dims 32*half + 8*grp .. +8, and the outer
+  // scales of keys 4*grp + i. Every page slot issues the same eight loads,
+  // so the wait for one buffer never covers the later buffers' loads in
+  // flight. Without a page to fetch they read this sequence's Q block
+  // instead (18 KB, read anyway, unused).
+  const uint32_t off_nib = row * kRec + 128 * half + 32 * grp;
+  const uint32_t off_sc = row * kRec + 256 + 16 * half + 4 * grp;
+  const uint32_t off_rp = row * kRec + 304 + 32 * half + 8 * grp;
+  const uint32_t off_s2 = 4 * grp * kRec + 292;
   const uint8_t *dummy = (const uint8_t *)(a.q + (size_t)qrow * a.hq * (kLat + 64));
-  auto fetch_from = [&](const uint8_t *page, PageRaw &r) {
-    r.nib[0] = __builtin_nontemporal_load((const v4u *)(page + off_nib));
-    r.nib[1] = __builtin_nontemporal_load((const v4u *)(page + off_nib + 8 * kRec));
-    r.tail = __builtin_nontemporal_load((const v4u *)(page + off_tail));
+  auto fetch_from = [&](const uint8_t *page, PageOp &r) {
+    r.nib[0] = *(const v4u *)(page + off_nib);
+    r.nib[1] = *(const v4u *)(page + off_nib + 16);
+    r.sc = *(const uint32_t *)(page + off_sc);
+    r.rp = *(const uint2 *)(page + off_rp);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.s2k[i] = *(const float *)(page + off_s2 + i * kRec);
   };
   // The first four page slots are requested before the Q work (page ids
   // from the wave's own copy), so that their latency overlaps Q's.
-  PageRaw bufs[kBufs];
+  PageOp bufs[kBufs];
 #pragma unroll
   for (int k = 0; k < kBufs; ++k) {
     const int p = p_begin + pair + k * kPairs;
@@ -248,6 +246,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     // multiplies them by P = 0
     for (int c = threadIdx.x; c < kXchOff / 16; c += kThreads) ((uint4 *)smem)[c] = make_uint4(0, 0, 0, 0);
     if (threadIdx.x < 2 * kPairs) (&s_flag[0][0])[threadIdx.x] = 0;
+    if (threadIdx.x == 0) s_err = 0;
     __syncthreads();
   }
   const float c_score = __builtin_ldexpf(a.scale_log2, -s_k[row]);   // undoes 2^k of head `row`
@@ -279,10 +278,6 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   const int rc1 = (row & 3) >> 1;
   const uint8_t *rbase = kt + 256 * rc1 + 16 * ((4 * grp + (row >> 2)) ^ (8 * rc1)) + 8 * (row & 1);
   v4f *xch = (v4f *)(smem + kXchOff) + pair * 2 * 2 * 64;   // [buf][half][lane]
-  uint8_t *st_nib = kt + kStageNib * (lane >> 3) + 16 * (lane & 7);          // + 8*kStageNib for load 1
-  uint8_t *st_tail = kt + kStageTail + kStageTailRow * (lane >> 2) + 16 * tch;
-  const uint8_t *ld_nib = kt + kStageNib * row + 32 * grp;
-  const uint8_t *ld_tail = kt + kStageTail + kStageTailRow * row;
 
   // Pair handshake: the exchange slots and K-row buffers are the pair's own,
   // so only the two waves of a pair meet per page. Each wave publishes a
@@ -302,28 +297,20 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     __asm__ volatile("" ::: "memory");
     if (lane == 0) *my_flag = n;
   };
+  bool stuck = false;
   auto pair_wait = [&](int n) {
-    while (*their_flag < n) __builtin_amdgcn_s_sleep(1);
+    for (int spins = 0; *their_flag < n;) {
+      if (++spins > kSpinLimit) {
+        stuck = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
     __asm__ volatile("" ::: "memory");
   };
-  auto fetch = [&](int p, PageRaw &r) {
+  auto fetch = [&](int p, PageOp &r) {
     fetch_from(p < p_end ? a.records + (size_t)__builtin_amdgcn_readfirstlane(s_bt[p - p_begin]) * (16 * kRec) : dummy,
                r);
-  };
-
-  // A page's bytes to the MFMA layout through the wave's staging area in
-  // K-row buffer kb (whose rows are no longer read).
-  auto stage = [&](const PageRaw &raw, int kb, PageOp &op) {
-    *(v4u *)(st_nib + kb) = raw.nib[0];
-    *(v4u *)(st_nib + kb + 8 * kStageNib) = raw.nib[1];
-    *(v4u *)(st_tail + kb) = raw.tail;
-    op.nib[0] = *(const v4u *)(ld_nib + kb);
-    op.nib[1] = *(const v4u *)(ld_nib + kb + 16);
-    op.sc = *(const uint32_t *)(ld_tail + kb + 4 * grp);
-    op.s2 = *(const float *)(ld_tail + kb + 16 + 4);
-    op.rp = *(const uint2 *)(ld_tail + kb + 32 + 8 * grp);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) op.s2k[i] = *(const float *)(kt + kb + kStageTail + kStageTailRow * (4 * grp + i) + 20);
   };
 
   // Softmax of page slot j (page p), one page later than its QK^T: the
@@ -371,11 +358,10 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   // p_end): the softmax of slot k-1; dequant + QK^T of page k (bytes in `op`)
   // into K-row buffer k&1, interleaved with the PV of page k-1 from the other
   // buffer; this wave's half scores of page k published for the partner; then
-  // the bytes of slot k+1 (`raw`) are staged into the other buffer into `op`,
-  // and `raw` is refilled with slot k+1+kBufs. Slots past p_end come last and
+  // `op` is refilled with slot k+kBufs. Slots past p_end come last and
   // publish nothing (neither wave of the pair reads their scores).
   float s2p_prev[4] = {0.f, 0.f, 0.f, 0.f};   // P scales of slot k-1
-  auto step = [&](PageOp &op, int k, PageRaw &raw) {
+  auto step = [&](PageOp &op, int k) {
     const int p = p_begin + pair + k * kPairs;
     const bool active = p < p_end;        // uniform over the wave
     const bool tail = (p + 1) * 16 > L;   // the sequence's last, partial page
@@ -387,22 +373,20 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     // scales (possibly NaN codes) and outer scales become zero, so their K
     // rows, V rows and P entries are exactly zero; their scores are masked.
     if (!active || tail) {
-      if (!active || p * 16 + row >= L) {
-        op.sc = 0u;
-        op.s2 = 0.0f;
-      }
+      if (!active || p * 16 + row >= L) op.sc = 0u;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (!active || p * 16 + 4 * grp + i >= L) op.s2k[i] = 0.0f;
     }
     // ---- outer-scale exponent of the pair (both waves see the same keys);
     // a raise rescales the accumulator after the previous page's PV
-    const int e2 = __builtin_amdgcn_frexp_expf(op.s2);
+    const float s2max = fmaxf(fmaxf(op.s2k[0], op.s2k[1]), fmaxf(op.s2k[2], op.s2k[3]));
+    const int e2 = __builtin_amdgcn_frexp_expf(s2max);
     int g_new = Gs;
-    if (__ballot(op.s2 > 0.0f && e2 > Gs)) {
-      int emax = op.s2 > 0.0f ? e2 : kGUnset;
-#pragma unroll
-      for (int msk = 1; msk < 16; msk <<= 1) emax = max(emax, __shfl_xor(emax, msk, 64));
+    if (__ballot(s2max > 0.0f && e2 > Gs)) {
+      int emax = s2max > 0.0f ? e2 : kGUnset;
+      emax = max(emax, __shfl_xor(emax, 16, 64));
+      emax = max(emax, __shfl_xor(emax, 32, 64));
       g_new = __builtin_amdgcn_readfirstlane(emax);
     }
     // ---- dequant + QK^T of this page, PV of the previous page
@@ -454,25 +438,20 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
       xch[(k & 1) * 128 + half * 64 + lane] = y;
       pair_publish(k + 1);
     }
-    // ---- next slot's bytes: staged into buffer (k+1)&1 (the PV above was
-    // its last reader); its load buffer is refilled right away
-    stage(raw, pbuf, op);
-    fetch(p + (kBufs + 1) * kPairs, raw);
+    // ---- this load buffer's next slot
+    fetch(p + kBufs * kPairs, op);
   };
 
   const int iters = p_end > p_begin ? (p_end - p_begin + kPairs - 1) / kPairs : 0;
-  PageOp op;
-  stage(bufs[0], 0, op);   // slot 0 into K-row buffer 0
-  fetch(p_begin + pair + kBufs * kPairs, bufs[0]);
-  // slot k sits in load buffer k % kBufs; step k stages slot k + 1
+  // slot k sits in load buffer k % kBufs
   int it = 0;
   for (; it + kBufs - 1 < iters; it += kBufs) {
 #pragma unroll
-    for (int j = 0; j < kBufs; ++j) step(op, it + j, bufs[(j + 1) % kBufs]);
+    for (int j = 0; j < kBufs; ++j) step(bufs[j], it + j);
   }
 #pragma unroll
   for (int j = 0; j < kBufs - 1; ++j)
-    if (it + j < iters) step(op, it + j, bufs[(j + 1) % kBufs]);
+    if (it + j < iters) step(bufs[j], it + j);
   // softmax and PV of the last page slot (K-row buffer (iters - 1) & 1; P is
   // zero if that slot held no page or there was none)
   {
@@ -494,6 +473,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   l_run += __shfl_xor(l_run, 32, 64);
   const bool has_o = m_run != -INFINITY && Gs != kGUnset;
   const float my_e = has_o ? m_run + (float)Gs : -INFINITY;
+  if (stuck) s_err = 1;
   if (half == 0 && grp == 0) {
     s_m[pair][row] = m_run;
     s_l[pair][row] = l_run;
@@ -527,6 +507,9 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     }
   }
   __syncthreads();
+  // a pair wait that gave up leaves NaN outputs (or NaN partials, which the
+  // combine turns into NaN outputs) rather than silently wrong values
+  const bool failed = s_err != 0;
   // output: 4 consecutive dims per thread and pass
   for (int e4 = threadIdx.x; e4 < kHeads * kLat / 4; e4 += kThreads) {
     const int hd = e4 / (kLat / 4);
@@ -551,10 +534,11 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
       uint2 w;
       w.x = f32_to_bf16_bits(acc[0] * sc) | (f32_to_bf16_bits(acc[1] * sc) << 16);
       w.y = f32_to_bf16_bits(acc[2] * sc) | (f32_to_bf16_bits(acc[3] * sc) << 16);
+      if (failed) w = make_uint2(0x7FC07FC0u, 0x7FC07FC0u);
       *(uint2 *)(a.out + ((size_t)qrow * a.hq + hd) * kLat + d) = w;
     } else {
       const size_t pi = ((size_t)b * a.hq + hd) * splits + split;
-      *(v4f *)(a.part_o + pi * kLat + d) = acc;
+      *(v4f *)(a.part_o + pi * kLat + d) = failed ? v4f{NAN, NAN, NAN, NAN} : acc;
       if (d == 0) *(v4f *)(a.part_ml + 4 * pi) = v4f{Mh, den, Eh, 0.0f};
     }
   }
