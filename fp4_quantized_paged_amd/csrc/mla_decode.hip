@@ -11,34 +11,33 @@
 // with Kt_j = e2m1 * e4m3(sg); out = sum_j p_j s2_j Kt_j / sum_j p_j.
 //
 // Kernel design (gfx950, wave64, one workgroup of 4 wave pairs per
-// (sequence, split); pairs take interleaved 16-key pages):
-//  * the two waves of a pair split the 512 latent dims (256 each) and the 64
-//    RoPE dims (32 each). Every product e2m1 * e4m3 is exact in fp16, so the
+// (sequence, split); each step of the workgroup covers 8 consecutive pages,
+// two per pair, one per wave):
+//  * every wave computes the whole QK^T and the softmax of its own page: the
 //    latent is dequantized by the hardware fp4 -> fp16 conversion and one
-//    packed fp16 multiply per two values. Q is held in registers as fp16,
-//    pre-scaled per head by a power of two that puts its largest element in
-//    [2^13, 2^14) (exact for all but elements 2^-31 below the head maximum);
-//  * QK^T on v_mfma_f32_16x16x32_f16 (A = 16 keys x 32 dims from registers,
-//    B = the 16 heads). The two half-dot-products meet through LDS (a
-//    handshake of the pair's two waves per page, no workgroup barrier);
-//    both waves then run the same softmax on identical scores;
-//  * the dequantized rows also go to LDS (chunk-major, bank-conflict free,
-//    two buffers per wave) and PV (v_mfma_f32_16x16x16_f16, A = V^T) reads
-//    them back with ds_read_b64_tr_b16, whose 16-lane transpose turns four
-//    row segments into one dim x 4 keys operand. The PV of page k-1 is
-//    interleaved with the dequant and QK^T of page k, so the vector ALU and
-//    the matrix cores work at the same time;
-//  * each wave keeps four pages of record bytes in flight, loaded straight
-//    into the MFMA operand layout (lane = key, 32 contiguous nibble bytes of
-//    its dim slice, the four group scales, eight RoPE codes, and the outer
-//    scales of the four keys whose scores the lane holds);
-//  * P enters PV in fp16. Per pair, Gs is the largest exponent of the outer
-//    scales seen so far; the keys' scales enter P as s2 * 2^-Gs < 1. Per head,
-//    the running max m is integer-valued and raised only when a score passes
-//    it by more than 8 (log2 units), so 2^(x - m) <= 2^8 and P stays far
-//    below the fp16 limit. The accumulator holds
-//    O_acc = 2^-Gs sum_j 2^(x_j - m) s2_j Kt_j; it is rescaled (by powers of
-//    two) only when m or Gs moves;
+//    packed fp16 multiply per two values (every e2m1 * e4m3 product is exact
+//    in fp16), and v_mfma_f32_16x16x32_f16 takes A = 16 keys x 32 dims from
+//    registers and B = the 16 heads' Q (fp16, pre-scaled per head by the power
+//    of two that puts its largest element in [2^13, 2^14); exact for all but
+//    elements 2^-31 below the head maximum);
+//  * the dequantized rows also go to LDS (16 KB per wave, chunk-major and
+//    bank-conflict free); after one workgroup barrier each wave of a pair
+//    takes half of the 512 latent dims of PV over both of the pair's pages:
+//    v_mfma_f32_16x16x32_f16 with A = V^T (two ds_read_b64_tr_b16 16-lane
+//    transposes, four keys of each page) and B = the two pages' P, which the
+//    pair exchanges through LDS in fp16. A second barrier per step keeps the
+//    rows until both halves have read them;
+//  * P enters PV in fp16 as 2^(x - m) * s2 * 2^-Gs. Per pair and head, the
+//    running max m is integer-valued and raised only when a score passes it
+//    by more than 8 (log2 units); Gs is the largest exponent of the outer
+//    scales seen, so P <= 2^8 and s2 * 2^-Gs < 1. Each wave raises m and Gs
+//    for its own page; after the exchange both waves take the larger values
+//    and rescale by powers of two (the accumulator, the denominator, and each
+//    page's P), so both halves of the pair hold the same m and Gs;
+//  * each wave keeps the record bytes of its next two pages in flight,
+//    loaded straight into the operand layout (lane = key, 64 contiguous
+//    nibble bytes, their 8 group scales, 16 RoPE codes, and the outer scales
+//    of the four keys whose scores the lane holds);
 //  * pairs merge through LDS; with one split the workgroup writes bf16, else
 //    (O, m, l, m + Gs) partials go to the workspace for the split combine.
 
@@ -54,25 +53,29 @@ constexpr int kWaves = 2 * kPairs;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRec = 368;
 constexpr int kLat = 512;
-constexpr int kHalf = 256;            // latent dims per wave
+constexpr int kHalf = 256;                        // latent dims of PV per wave
 constexpr int kHeads = 16;
-constexpr int kKtBytes = 16 * kHalf * 2;          // fp16 K rows of one page, one wave
+constexpr int kRowBytes = 16 * kLat * 2;          // fp16 latent rows of one page
 constexpr int kStageRowU4 = (kLat + 64) / 8 + 1;  // bf16 Q staging row, uint4 units
 constexpr float kTau = 8.0f;                      // lazy-max slack, log2 units
 constexpr int kGUnset = -(1 << 20);               // Gs before any nonzero outer scale
 constexpr int kSlabRow = kHalf + 4;               // merge slab row (floats, padded)
 constexpr int kBtPerThread = 4;                   // block-table entries staged per thread
 constexpr int kMaxSplitPages = kBtPerThread * kThreads;   // pages of one split (2,048)
-constexpr int kBufs = 4;                          // pages of record bytes in flight per wave (5 or 6: slower)
+constexpr int kBufs = 2;                          // pages of record bytes in flight per wave
+constexpr int kStepPages = kWaves;                // pages per workgroup step
+// Spins of a pair wait before the wave gives up (each spin sleeps ~64
+// cycles; a normal wait takes a few spins).
+constexpr int kSpinLimit = 1 << 22;
+constexpr int kQReg = 4;                          // latent QK^T steps whose Q operand stays in registers
+constexpr int kQLds = 16 + 2 - kQReg;             // the other latent steps and the 2 RoPE steps: from LDS
 
-// LDS: two K-row buffers per wave, then the pair exchange. Before the loop
-// the first region holds the staged bf16 Q; after it, the merge slabs.
-constexpr int kXchOff = kWaves * 2 * kKtBytes;
-constexpr int kXchBytes = kPairs * 2 * 2 * 64 * 16;
-constexpr int kSmemBytes = kXchOff + kXchBytes;
-static_assert(2 * 2 * kHeads * kSlabRow * 4 <= kXchOff, "merge slabs fit");
+// LDS: the latent rows of each wave's page. Before the loop the region holds
+// the staged bf16 Q; after it, the merge slabs.
+constexpr int kRowsBytes = kWaves * kRowBytes;
+static_assert(2 * 2 * kHeads * kSlabRow * 4 <= kRowsBytes, "merge slabs fit");
 static_assert(((kHeads * (kLat + 64) / 8 + kThreads - 1) / kThreads * kThreads / ((kLat + 64) / 8) + 1) *
-                  kStageRowU4 * 16 <= kXchOff,
+                  kStageRowU4 * 16 <= kRowsBytes,
               "staged Q, with the prologue's spill-over rows, fits");
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
@@ -117,106 +120,109 @@ __device__ __forceinline__ uint32_t bf16x2_absmax(uint32_t w) {
 
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
 
-// One wave's share of a page's record bytes, loaded in the MFMA layout
-// (lane = key `row`, dim group `grp`).
+// 2^e as fp32 for an integer-valued e (0 below 2^-200)
+__device__ __forceinline__ float pow2i(float e) { return __builtin_ldexpf(1.0f, max((int)e, -200)); }
+
+// The record bytes of one page that a wave needs, in the MFMA layout (lane =
+// key `row`, dim group `grp`).
 struct PageOp {
-  v4u nib[2];      // e2m1 codes of dims 64*grp .. +64 of the wave's 256
-  uint32_t sc;     // their four group scales
-  uint2 rp;        // RoPE codes of dims 32*half + 8*grp .. +8
-  float s2k[4];    // outer scales of keys 4*grp + i (this lane's scores)
+  v4u nib[4];      // e2m1 codes of latent dims 128*grp .. +128
+  uint2 sc;        // their 8 group scales
+  v4u rp;          // RoPE codes of dims 16*grp .. +16
+  float s2;        // outer scale of key 4*grp + row%4 (its quad holds keys 4*grp .. +4)
 };
 
-// Spins of a pair wait before the wave gives up (each spin sleeps ~64
-// cycles; a normal wait takes a few spins). A wave that gives up marks the
-// workgroup and its outputs become NaN instead of the kernel hanging.
-constexpr int kSpinLimit = 1 << 22;
-
 __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a, int splits, int pages_per_split) {
-  __shared__ __align__(16) uint8_t smem[kSmemBytes];
-  __shared__ float s_m[kPairs][kHeads], s_l[kPairs][kHeads], s_e[kPairs][kHeads];
+  __shared__ __align__(16) uint8_t smem[kRowsBytes];
+  __shared__ uint2 s_p[kWaves][64];                   // each wave's P of its page (fp16 x 4 per lane)
+  __shared__ float s_mp[kWaves][kHeads];              // the m that P was taken against
+  __shared__ int s_gp[kWaves];                        // the Gs that P was taken against
+  __shared__ float s_m[kPairs][kHeads], s_e[kPairs][kHeads], s_l[kWaves][kHeads];
   __shared__ int s_k[kHeads];
-  __shared__ int s_flag[kPairs][2];                    // pages whose half scores are published
-  __shared__ int s_err;                                // a pair wait gave up
-  __shared__ int s_bt[kMaxSplitPages];                 // this split's block-table slice
+  __shared__ int s_flag[kWaves];                      // pair handshake counters
+  __shared__ int s_err;                               // a pair wait gave up
+  __shared__ int s_bt[kMaxSplitPages];                // this split's block-table slice
+  __shared__ uint4 s_q[kQLds][64];                    // fp16 Q operands of steps kQReg .. 17, per lane
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the two waves of a pair are neighbours (different SIMDs); every SIMD
+  // carries waves of two pairs, which need not be in the same phase
   const int pair = wave >> 1;
   const int half = wave & 1;
-  const int row = lane & 15;      // key of the A operand / head of the output
+  const int partner = wave ^ 1;
+  const int wpos = 2 * pair + half;   // this wave's page within a step
+  const int row = lane & 15;          // key of the A operand / head of the output
   const int grp = lane >> 4;
   // work item: (sequence b, split); the query is row b
   const int b = blockIdx.x / splits;
   const int split = blockIdx.x - b * splits;
-  const int L = a.seq_lens[b];
   const int qrow = b;
-  const int npages = (L + 15) >> 4;
   const int p_begin = split * pages_per_split;
-  const int p_end = min(npages, p_begin + pages_per_split);
   const int32_t *bt = a.block_table + (size_t)b * a.bt_stride;
-  const int nbt = p_end - p_begin;   // at most kMaxSplitPages
-  // Page ids first (clamped indexes keep the loads unconditional): this
-  // wave's copy of the split's first 64, and the split's block-table slice
-  // (one entry per thread).
-  const int btw = bt[p_begin + max(0, min(lane, nbt - 1))];
+  const int bt_last = (int)a.bt_stride - 1;
+  // Sequence length, page ids and Q are requested together: the block-table
+  // reads are clamped to the table row, not to the sequence, so they need no
+  // length (entries past the sequence are never used as addresses).
+  const int L = a.seq_lens[b];
+  const int btw = bt[min(p_begin + lane, bt_last)];
   int btt[kBtPerThread];
 #pragma unroll
-  for (int j = 0; j < kBtPerThread; ++j)
-    btt[j] = bt[p_begin + max(0, min((int)threadIdx.x + j * kThreads, nbt - 1))];
-  __builtin_amdgcn_sched_barrier(0);
+  for (int j = 0; j < kBtPerThread; ++j) btt[j] = bt[min(p_begin + (int)threadIdx.x + j * kThreads, bt_last)];
+  constexpr int kQU4 = kHeads * (kLat + 64) / 8;
+  constexpr int kQPer = (kQU4 + kThreads - 1) / kThreads;
+  const uint4 *qsrc = (const uint4 *)(a.q + (size_t)qrow * a.hq * (kLat + 64));
+  uint4 qv[kQPer];
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) qv[j] = qsrc[min((int)threadIdx.x + j * kThreads, kQU4 - 1)];
+  const int npages = (L + 15) >> 4;
+  const int p_end = min(npages, p_begin + pages_per_split);
+  const int nsteps = p_end > p_begin ? (p_end - p_begin + kStepPages - 1) / kStepPages : 0;
 
   // Operand loads, per lane: key `row` of the page at byte 368*row; the
-  // nibbles of dims 256*half + 64*grp .. +64 (32 bytes), their group scales
-  // (4 bytes), the RoPE codes of dims 32*half + 8*grp .. +8, and the outer
-  // scales of keys 4*grp + i. Every page slot issues the same eight loads,
-  // so the wait for one buffer never covers the later buffers' loads in
-  // flight. Without a page to fetch they read this sequence's Q block
-  // instead (18 KB, read anyway, unused).
-  const uint32_t off_nib = row * kRec + 128 * half + 32 * grp;
-  const uint32_t off_sc = row * kRec + 256 + 16 * half + 4 * grp;
-  const uint32_t off_rp = row * kRec + 304 + 32 * half + 8 * grp;
-  const uint32_t off_s2 = 4 * grp * kRec + 292;
-  const uint8_t *dummy = (const uint8_t *)(a.q + (size_t)qrow * a.hq * (kLat + 64));
-  auto fetch_from = [&](const uint8_t *page, PageOp &r) {
-    r.nib[0] = *(const v4u *)(page + off_nib);
-    r.nib[1] = *(const v4u *)(page + off_nib + 16);
-    r.sc = *(const uint32_t *)(page + off_sc);
-    r.rp = *(const uint2 *)(page + off_rp);
+  // nibbles of latent dims 128*grp .. +128 (64 bytes), their 8 group scales,
+  // the RoPE codes of dims 16*grp .. +16, and the outer scale of key
+  // 4*grp + row%4 (a quad broadcast gives each lane the outer scales of the
+  // four keys whose scores it holds). Raw buffer loads: the page address sits
+  // in the scalar resource and each lane adds its constant 32-bit offset; a
+  // slot without a page gets a resource of zero bytes, whose loads return 0.
+  const uint32_t off_nib = row * kRec + 64 * grp;
+  const uint32_t off_sc = row * kRec + 256 + 8 * grp;
+  const uint32_t off_rp = row * kRec + 304 + 16 * grp;
+  const uint32_t off_s2 = (4 * grp + (row & 3)) * kRec + 292;
+  auto fetch_page = [&](bool act, int ph, PageOp &r) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.records + (size_t)(act ? ph : 0) * (16 * kRec)), (short)0, act ? 16 * kRec : 0, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.s2k[i] = *(const float *)(page + off_s2 + i * kRec);
+    for (int i = 0; i < 4; ++i) r.nib[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off_nib + 16 * i, 0, 0);
+    r.sc = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off_sc, 0, 0));
+    r.rp = __builtin_amdgcn_raw_buffer_load_b128(rs, off_rp, 0, 0);
+    r.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off_s2, 0, 0));
   };
-  // The first four page slots are requested before the Q work (page ids
-  // from the wave's own copy), so that their latency overlaps Q's.
   PageOp bufs[kBufs];
 #pragma unroll
   for (int k = 0; k < kBufs; ++k) {
-    const int p = p_begin + pair + k * kPairs;
-    const int ph = __builtin_amdgcn_readlane(btw, pair + k * kPairs);   // a clamped copy past the split
-    fetch_from(p < p_end ? a.records + (size_t)ph * (16 * kRec) : dummy, bufs[k]);
+    const int p = p_begin + kStepPages * k + wpos;
+    fetch_page(p < p_end, __builtin_amdgcn_readlane(btw, kStepPages * k + wpos), bufs[k]);
   }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- Q: stage bf16 in LDS, find each head's power-of-two scale k (largest
-  // element of head h times 2^k in [2^13, 2^14)), keep this lane's operands
-  // (head `row`; latent step c: dims 256*half + 64*grp + 8c; RoPE: dims
-  // 512 + 32*half + 8*grp) as fp16 Q * 2^k in registers
-  uint4 qop[8], qrope;
+  // element of head h times 2^k in [2^13, 2^14)), and form this lane's
+  // operands (head `row`; latent step c: dims 128*grp + 8c; RoPE step u:
+  // dims 512 + 16*grp + 8u) as fp16 Q * 2^k: the first kQReg latent steps in
+  // registers, the rest in LDS (the same for every wave, written once)
+  uint4 qop[kQReg];
   {
-    // Q is requested behind the first pages, so both arrive in one round trip
-    constexpr int kQU4 = kHeads * (kLat + 64) / 8;
-    const uint4 *qsrc = (const uint4 *)(a.q + (size_t)qrow * a.hq * (kLat + 64));
-    uint4 qv[(kQU4 + kThreads - 1) / kThreads];
 #pragma unroll
-    for (int j = 0; j < (kQU4 + kThreads - 1) / kThreads; ++j)
-      qv[j] = qsrc[min((int)threadIdx.x + j * kThreads, kQU4 - 1)];
-#pragma unroll
-    for (int j = 0; j < kBtPerThread; ++j)
-      if ((int)threadIdx.x + j * kThreads < nbt) s_bt[threadIdx.x + j * kThreads] = btt[j];
+    for (int j = 0; j < kBtPerThread; ++j) s_bt[threadIdx.x + j * kThreads] = btt[j];
+    if (threadIdx.x < kWaves) s_flag[threadIdx.x] = 0;
+    if (threadIdx.x == 0) s_err = 0;
     uint4 *qs = (uint4 *)smem;
-    // unconditional stores: entries past Q (rows 16 .. 21) land in K-row
-    // buffer space that is cleared below
+    // unconditional stores: entries past Q (rows 16 .. 21) land in row space
+    // that is overwritten before it is read
 #pragma unroll
-    for (int j = 0; j < (kQU4 + kThreads - 1) / kThreads; ++j) {
+    for (int j = 0; j < kQPer; ++j) {
       const int c = threadIdx.x + j * kThreads;
       const int h = c / ((kLat + 64) / 8);
       qs[h * kStageRowU4 + (c - h * ((kLat + 64) / 8))] = qv[j];
@@ -239,65 +245,62 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     const uint4 *qr = qs + row * kStageRowU4;
     const int k = s_k[row];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) qop[c] = bf16x8_to_f16(qr[(kHalf * half + 64 * grp + 8 * c) / 8], k);
-    qrope = bf16x8_to_f16(qr[(kLat + 32 * half + 8 * grp) / 8], k);
-    __syncthreads();
-    // K-row buffers start at zero: the PV of a page slot that holds no page
-    // multiplies them by P = 0
-    for (int c = threadIdx.x; c < kXchOff / 16; c += kThreads) ((uint4 *)smem)[c] = make_uint4(0, 0, 0, 0);
-    if (threadIdx.x < 2 * kPairs) (&s_flag[0][0])[threadIdx.x] = 0;
-    if (threadIdx.x == 0) s_err = 0;
-    __syncthreads();
+    for (int c = 0; c < kQReg; ++c) qop[c] = bf16x8_to_f16(qr[16 * grp + c], k);
+    for (int j = wave; j < kQLds; j += kWaves) {
+      const int c = kQReg + j;
+      s_q[j][lane] = bf16x8_to_f16(qr[c < 16 ? 16 * grp + c : (kLat + 16 * grp + 8 * (c - 16)) / 8], k);
+    }
   }
+  __syncthreads();   // staged Q read, s_q written, flags cleared: rows may be written
   const float c_score = __builtin_ldexpf(a.scale_log2, -s_k[row]);   // undoes 2^k of head `row`
   const float c_rope = a.rope_scale * c_score;
 
-  // per head `row`: running integer max m (log2 units) and this lane's part
-  // of the denominator; per pair: the outer-scale exponent Gs. The
-  // accumulator holds O_acc = 2^-Gs * sum_j 2^(x_j - m) s2_j Kt_j.
+  // Pair state, equal in both waves: per head `row` the running integer max
+  // m (log2 units); the outer-scale exponent Gs. Per wave: this lane's part
+  // of the denominator of the wave's own pages (relative to m). The
+  // accumulator holds O_acc = 2^-Gs * sum_j 2^(x_j - m) s2_j Kt_j over the
+  // pair's pages, for dims 256*half .. +256.
   float m_run = -INFINITY;
   float l_run = 0.0f;
   int Gs = kGUnset;
   v4f o[16];
 #pragma unroll
   for (int t = 0; t < 16; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
-  v4h pb_prev = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};   // P of the previous page
 
-  // K rows, chunk-major: 16-byte chunk ch (dims 8ch .. 8ch+7 of the wave's
-  // 256) of key r sits at 256*ch + 16*(r ^ 8*(ch&1)). Row writes (8 or 16
+  // Latent rows, chunk-major: 16-byte chunk ch (dims 8ch .. 8ch+7) of key r
+  // sits at 256*ch + 16*(r ^ 8*(ch&1)) of the wave's 16 KB. Row writes (16
   // keys of one chunk) cover distinct banks; a transposed read serves 32
-  // lanes (keys 0-7 or 8-15 of chunks 2q and 2q+1) per pass, and the XOR
-  // puts the odd chunk's half of them in the other 128 bytes, so the pass
-  // covers all 64 banks once (XOR 4 had left both chunks' keys on the same
-  // 32 banks, a 2-way conflict). Buffer j of the wave is kKtBytes further.
-  uint8_t *kt = smem + wave * 2 * kKtBytes;
-  uint8_t *wbase_e = kt + 2048 * grp + 16 * row;          // even steps: chunk 8*grp + c
-  uint8_t *wbase_o = kt + 2048 * grp + 16 * (row ^ 8);    // odd steps
+  // lanes (keys 0-7 or 8-15 of chunks 2q and 2q+1) per pass, and the XOR puts
+  // the odd chunk's half of them in the other 128 bytes, so the pass covers
+  // all 64 banks once.
+  uint8_t *myrows = smem + wave * kRowBytes;
+  uint8_t *wbase_e = myrows + 4096 * grp + 16 * row;          // even steps c: chunk 16*grp + c
+  uint8_t *wbase_o = myrows + 4096 * grp + 16 * (row ^ 8);    // odd steps
   // transposed reads: lane s of group grp reads key 4*grp + s/4, dims
-  // 16q + 4(s%4) .. +4 = chunk 2q + (s%4)/2, 8-byte half (s%4)&1
+  // 16q + 4(s%4) .. +4 = chunk 2q + (s%4)/2, 8-byte half (s%4)&1; tile q of
+  // this wave's dim half is 512*(16*half + q) further
   const int rc1 = (row & 3) >> 1;
-  const uint8_t *rbase = kt + 256 * rc1 + 16 * ((4 * grp + (row >> 2)) ^ (8 * rc1)) + 8 * (row & 1);
-  v4f *xch = (v4f *)(smem + kXchOff) + pair * 2 * 2 * 64;   // [buf][half][lane]
+  const int rd_off = 256 * rc1 + 16 * ((4 * grp + (row >> 2)) ^ (8 * rc1)) + 8 * (row & 1) + 8192 * half;
+  const uint8_t *rd0 = smem + (2 * pair) * kRowBytes + rd_off;       // page of the pair's half-0 wave
+  const uint8_t *rd1 = smem + (2 * pair + 1) * kRowBytes + rd_off;   // page of its half-1 wave
 
-  // Pair handshake: the exchange slots and K-row buffers are the pair's own,
-  // so only the two waves of a pair meet per page. Each wave publishes a
-  // page counter after its half scores of an active slot and, one step
-  // later, waits for its partner's counter of that slot; LDS operations of
-  // one wave complete in issue order, so a counter that reads n means the
-  // partner's scores of slot n - 1 are in place. Both waves run the same
-  // slots and publish slot j before they wait for slot j, so every wait
-  // ends. A wave overwrites the exchange slot of j only late in slot j + 2,
-  // after waiting (early in slot j + 2) for the partner's counter j + 2,
-  // which the partner publishes late in its slot j + 1, after its reads of
-  // slot j early in that slot.
+  // Pair handshake through LDS counters. Step k: a wave publishes 2k+1 once
+  // its rows and P are written, and 2k+2 once its PV has read the partner's
+  // rows and P; before writing rows of step k it waits for the partner's 2k,
+  // before its PV for the partner's 2k+1. LDS operations of one wave complete
+  // in issue order, so a counter read as n means everything the partner
+  // wrote before publishing n is in place. Each wait is for a value the
+  // partner publishes before its own wait for the same value, so every wait
+  // ends; a wave that spins past the limit marks the workgroup (NaN outputs)
+  // instead of hanging.
   typedef __attribute__((address_space(3))) volatile int lds_int;
-  lds_int *my_flag = (lds_int *)&s_flag[pair][half];
-  lds_int *their_flag = (lds_int *)&s_flag[pair][half ^ 1];
+  lds_int *my_flag = (lds_int *)&s_flag[wave];
+  lds_int *their_flag = (lds_int *)&s_flag[partner];
+  bool stuck = false;
   auto pair_publish = [&](int n) {
     __asm__ volatile("" ::: "memory");
     if (lane == 0) *my_flag = n;
   };
-  bool stuck = false;
   auto pair_wait = [&](int n) {
     for (int spins = 0; *their_flag < n;) {
       if (++spins > kSpinLimit) {
@@ -308,183 +311,195 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     }
     __asm__ volatile("" ::: "memory");
   };
-  auto fetch = [&](int p, PageOp &r) {
-    fetch_from(p < p_end ? a.records + (size_t)__builtin_amdgcn_readfirstlane(s_bt[p - p_begin]) * (16 * kRec) : dummy,
-               r);
+
+  auto fetch = [&](int k, PageOp &r) {
+    const int p = p_begin + kStepPages * k + wpos;
+    const bool act = p < p_end;
+    fetch_page(act, act ? __builtin_amdgcn_readfirstlane(s_bt[p - p_begin]) : 0, r);
   };
 
-  // Softmax of page slot j (page p), one page later than its QK^T: the
-  // partner's half scores of slot j were published a whole step earlier, so
-  // the wait for them almost never stalls. Sets pb_prev = P of slot j.
-  auto softmax_of = [&](int j, int p, const float (&s2p)[4]) {
-    const bool tail = (p + 1) * 16 > L;
-    pair_wait(j + 1);
-    const v4f y0 = xch[(j & 1) * 128 + lane];
-    const v4f y1 = xch[(j & 1) * 128 + 64 + lane];
+  // Step k: page p = p_begin + 8k + wpos of this wave.
+  auto step = [&](PageOp &op, int k) {
+    const int p = p_begin + kStepPages * k + wpos;
+    // a page past the split, or the sequence's last, partial page: some or
+    // all keys masked (uniform over the wave)
+    const bool tail = p >= p_end || (p + 1) * 16 > L;
+    const int kend = p < p_end ? L - p * 16 : 0;   // keys of the page that exist
+    // Keys past the end, and every key of a slot without a page: group
+    // scales (possibly NaN codes) and outer scales become zero, so their rows
+    // and P entries are exactly zero; their scores are masked.
+    // outer scales of keys 4*grp + i: quad_perm broadcasts of lane i of the quad
+    const int s2b = __builtin_bit_cast(int, op.s2);
+    float s2k[4] = {__builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(s2b, 0x00, 0xF, 0xF, false)),
+                    __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(s2b, 0x55, 0xF, 0xF, false)),
+                    __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(s2b, 0xAA, 0xF, 0xF, false)),
+                    __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(s2b, 0xFF, 0xF, 0xF, false))};
+    if (tail) {
+      if (row >= kend) op.sc = make_uint2(0u, 0u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * grp + i >= kend) s2k[i] = 0.0f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pair_wait(2 * k);   // the partner's PV of the previous step has read these rows
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- dequant + rows + QK^T of this wave's page (two accumulators)
+    v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = acc0, accr = acc0;
+    const v2h sg[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(op.sc.x, 1.0f, false),
+                       __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(op.sc.x, 1.0f, true),
+                       __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(op.sc.y, 1.0f, false),
+                       __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(op.sc.y, 1.0f, true)};
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const _Float16 s = sg[c >> 2][(c >> 1) & 1];   // group 8*grp + c/2
+      const uint4 x = fp4x8_f16(op.nib[c >> 2][c & 3], v2h{s, s});
+      *(uint4 *)(((c & 1) ? wbase_o : wbase_e) + 256 * c) = x;
+      const uint4 qc = c < kQReg ? qop[c < kQReg ? c : 0] : s_q[c < kQReg ? 0 : c - kQReg][lane];
+      if (c & 1)
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, x), __builtin_bit_cast(v8h, qc), acc1,
+                                                      0, 0, 0);
+      else
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, x), __builtin_bit_cast(v8h, qc), acc0,
+                                                      0, 0, 0);
+      // one step's dequant in registers at a time (the scheduler would
+      // otherwise batch them)
+      if (c & 1) __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint4 xr = e4m3x8_f16(u == 0 ? make_uint2(op.rp.x, op.rp.y) : make_uint2(op.rp.z, op.rp.w));
+      accr = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xr),
+                                                    __builtin_bit_cast(v8h, s_q[16 - kQReg + u][lane]), accr, 0, 0, 0);
+    }
+    // ---- log2-domain scores of keys 4*grp + i, head `row`; softmax of the
+    // page against the pair's m and Gs, raised for this page if needed
     float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = y0[i] + y1[i];
+    for (int i = 0; i < 4; ++i) x[i] = fmaf(c_score * s2k[i], acc0[i] + acc1[i], c_rope * accr[i]);
     if (tail) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (p * 16 + 4 * grp + i >= L) x[i] = -INFINITY;
+        if (4 * grp + i >= kend) x[i] = -INFINITY;
     }
+    float m_self = m_run;
     bool raise_m = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) raise_m |= x[i] > m_run + kTau;
     if (__ballot(raise_m)) {
       float bmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       bmax = xor_max(xor_max(bmax, 16), 32);
-      if (bmax > m_run + kTau) {
-        const float m_new = __builtin_ceilf(bmax);
-        const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);   // power of two
-        l_run *= alpha;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) o[q] *= alpha;
-        m_run = m_new;
+      if (bmax > m_run + kTau) m_self = __builtin_ceilf(bmax);
+    }
+    int g_self = Gs;
+    {
+      const float s2max = fmaxf(fmaxf(s2k[0], s2k[1]), fmaxf(s2k[2], s2k[3]));
+      const int e2 = __builtin_amdgcn_frexp_expf(s2max);
+      if (__ballot(s2max > 0.0f && e2 > Gs)) {
+        int emax = s2max > 0.0f ? e2 : kGUnset;
+        emax = max(emax, __shfl_xor(emax, 16, 64));
+        emax = max(emax, __shfl_xor(emax, 32, 64));
+        g_self = max(Gs, __builtin_amdgcn_readfirstlane(emax));
       }
     }
-    float pw[4];
+    float pe[4];
+    float psum = 0.0f;
+    v4h pw;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float pe = __builtin_amdgcn_exp2f(x[i] - m_run);   // <= 2^8
-      l_run += pe;
-      pw[i] = pe * s2p[i];
+      pe[i] = m_self == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[i] - m_self);   // <= 2^8
+      psum += pe[i];
+      pw[i] = (_Float16)(pe[i] * __builtin_ldexpf(s2k[i], -g_self));           // s2 * 2^-Gs < 1
     }
-    pb_prev = v4h{(_Float16)pw[0], (_Float16)pw[1], (_Float16)pw[2], (_Float16)pw[3]};
-  };
-
-  // Page slot k of this pair (page p = p_begin + pair + k*kPairs, if below
-  // p_end): the softmax of slot k-1; dequant + QK^T of page k (bytes in `op`)
-  // into K-row buffer k&1, interleaved with the PV of page k-1 from the other
-  // buffer; this wave's half scores of page k published for the partner; then
-  // `op` is refilled with slot k+kBufs. Slots past p_end come last and
-  // publish nothing (neither wave of the pair reads their scores).
-  float s2p_prev[4] = {0.f, 0.f, 0.f, 0.f};   // P scales of slot k-1
-  auto step = [&](PageOp &op, int k) {
-    const int p = p_begin + pair + k * kPairs;
-    const bool active = p < p_end;        // uniform over the wave
-    const bool tail = (p + 1) * 16 > L;   // the sequence's last, partial page
-    const int cb = (k & 1) * kKtBytes;    // this page's K-row buffer
-    const int pbuf = kKtBytes - cb;       // the previous page's, and the next's
-    pb_prev = v4h{(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
-    if (k > 0 && p - kPairs < p_end) softmax_of(k - 1, p - kPairs, s2p_prev);
-    // Keys past the end, and every key of a slot without a page: group
-    // scales (possibly NaN codes) and outer scales become zero, so their K
-    // rows, V rows and P entries are exactly zero; their scores are masked.
-    if (!active || tail) {
-      if (!active || p * 16 + row >= L) op.sc = 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (!active || p * 16 + 4 * grp + i >= L) op.s2k[i] = 0.0f;
-    }
-    // ---- outer-scale exponent of the pair (both waves see the same keys);
-    // a raise rescales the accumulator after the previous page's PV
-    const float s2max = fmaxf(fmaxf(op.s2k[0], op.s2k[1]), fmaxf(op.s2k[2], op.s2k[3]));
-    const int e2 = __builtin_amdgcn_frexp_expf(s2max);
-    int g_new = Gs;
-    if (__ballot(s2max > 0.0f && e2 > Gs)) {
-      int emax = s2max > 0.0f ? e2 : kGUnset;
-      emax = max(emax, __shfl_xor(emax, 16, 64));
-      emax = max(emax, __shfl_xor(emax, 32, 64));
-      g_new = __builtin_amdgcn_readfirstlane(emax);
-    }
-    // ---- dequant + QK^T of this page, PV of the previous page
-    const v2h sg01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(op.sc, 1.0f, false);
-    const v2h sg23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(op.sc, 1.0f, true);
-    v4f acc_l = v4f{0.f, 0.f, 0.f, 0.f};
-    // PV operand reads run kLook tiles ahead of their MFMAs (2, 8 and 16
-    // measured within 1% of each other)
-    constexpr int kLook = 8;
-    v4s va[16];
+    s_p[wave][lane] = __builtin_bit_cast(uint2, pw);
+    if (grp == 0) s_mp[wave][row] = m_self;
+    if (lane == 0) s_gp[wave] = g_self;
+    pair_publish(2 * k + 1);
+    // ---- this load buffer's next page
+    fetch(k + kBufs, op);
+    __builtin_amdgcn_sched_barrier(0);
+    pair_wait(2 * k + 1);   // the partner's rows and P of the step are in place
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- PV over the pair's two pages, this wave's half of the latent
+    v4h pother = __builtin_bit_cast(v4h, s_p[partner][lane]);
+    const float m_other = s_mp[partner][row];
+    const int g_other = s_gp[partner];
+    constexpr int kLook = 4;   // operand reads in flight ahead of their MFMAs
+    v4s va0[16], va1[16];
     auto read_tile = [&](int q) {
-      va[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(rbase + pbuf + 512 * q));
+      va0[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(rd0 + 512 * q));
+      va1[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(rd1 + 512 * q));
     };
 #pragma unroll
     for (int q = 0; q < kLook; ++q) read_tile(q);
+    // the pair's common m and Gs after this step; rescales are powers of two
+    const float m_new = fmaxf(m_self, m_other);
+    const int g_new = max(g_self, g_other);
+    if (__ballot(m_new != m_run || g_new != Gs)) {
+      const float e_new = m_new + (float)g_new;
+      const float f_o = (m_run == -INFINITY || Gs == kGUnset) ? 0.0f : pow2i(m_run + (float)Gs - e_new);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        if (2 * c + j + kLook < 16) read_tile(2 * c + j + kLook);
-      const _Float16 s = (c >> 2) == 0 ? sg01[(c >> 1) & 1] : sg23[(c >> 1) & 1];
-      const uint4 x = fp4x8_f16(op.nib[c >> 2][c & 3], v2h{s, s});
-      *(uint4 *)(((c & 1) ? wbase_o : wbase_e) + cb + 256 * c) = x;
-      acc_l = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, x), __builtin_bit_cast(v8h, qop[c]),
-                                                     acc_l, 0, 0, 0);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int q = 2 * c + j;   // PV tile: dims 16q .. 16q+15
-        o[q] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h, va[q]), pb_prev, o[q], 0, 0, 0);
-      }
-    }
-    const uint4 xr = e4m3x8_f16(op.rp);
-    const v4f acc_r = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, xr), __builtin_bit_cast(v8h, qrope),
-                                                             v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-    if (g_new != Gs) {
-      const float f = __builtin_ldexpf(1.0f, max(Gs - g_new, -200));
-#pragma unroll
-      for (int q = 0; q < 16; ++q) o[q] *= f;
-      Gs = g_new;
-    }
-    // this wave's part of the log2-domain scores of keys 4*grp + i, head `row`
-    if (active) {
-      v4f y;
+      for (int t = 0; t < 16; ++t) o[t] *= f_o;
+      l_run = (m_run == -INFINITY ? 0.0f : l_run * pow2i(m_run - m_new)) +
+              (m_self == -INFINITY ? 0.0f : psum * pow2i(m_self - m_new));
+      const float f_self = (m_self == -INFINITY || g_self == kGUnset) ? 0.0f : pow2i(m_self + (float)g_self - e_new);
+      const float f_other =
+          (m_other == -INFINITY || g_other == kGUnset) ? 0.0f : pow2i(m_other + (float)g_other - e_new);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        y[i] = fmaf(c_score * op.s2k[i], acc_l[i], c_rope * acc_r[i]);
-        s2p_prev[i] = __builtin_ldexpf(op.s2k[i], -Gs);   // < 1
+        pw[i] = (_Float16)((float)pw[i] * f_self);
+        pother[i] = (_Float16)((float)pother[i] * f_other);
       }
-      xch[(k & 1) * 128 + half * 64 + lane] = y;
-      pair_publish(k + 1);
+      m_run = m_new;
+      Gs = g_new;
+    } else {
+      l_run += psum;
     }
-    // ---- this load buffer's next slot
-    fetch(p + kBufs * kPairs, op);
+    const v4h p0 = half == 0 ? pw : pother;
+    const v4h p1 = half == 0 ? pother : pw;
+    const v8h pb = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (q + kLook < 16) read_tile(q + kLook);
+      const v8h va = __builtin_shufflevector(__builtin_bit_cast(v4h, va0[q]), __builtin_bit_cast(v4h, va1[q]), 0, 1,
+                                             2, 3, 4, 5, 6, 7);
+      o[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, o[q], 0, 0, 0);
+      // keep the reads kLook tiles ahead instead of letting the scheduler
+      // hoist all of them (64 registers)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pair_publish(2 * k + 2);
   };
 
-  const int iters = p_end > p_begin ? (p_end - p_begin + kPairs - 1) / kPairs : 0;
-  // slot k sits in load buffer k % kBufs
+  // page slot k sits in load buffer k % kBufs
   int it = 0;
-  for (; it + kBufs - 1 < iters; it += kBufs) {
+  for (; it + kBufs - 1 < nsteps; it += kBufs) {
 #pragma unroll
     for (int j = 0; j < kBufs; ++j) step(bufs[j], it + j);
   }
 #pragma unroll
   for (int j = 0; j < kBufs - 1; ++j)
-    if (it + j < iters) step(bufs[j], it + j);
-  // softmax and PV of the last page slot (K-row buffer (iters - 1) & 1; P is
-  // zero if that slot held no page or there was none)
-  {
-    pb_prev = v4h{(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
-    const int p_last = p_begin + pair + (iters - 1) * kPairs;
-    if (iters > 0 && p_last < p_end) softmax_of(iters - 1, p_last, s2p_prev);
-    const int pbuf = ((iters - 1) & 1) * kKtBytes;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const v4s va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s *)(rbase + pbuf + 512 * q));
-      o[q] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h, va), pb_prev, o[q], 0, 0, 0);
-    }
-  }
+    if (it + j < nsteps) step(bufs[j], it + j);
 
-  // ---- merge the pairs. Pair totals per head: l_abs = 2^m l,
-  // O_abs = 2^(m + Gs) O_acc.
+  // ---- merge the pairs. Pair totals per head: l_abs = 2^m (l_half0 +
+  // l_half1), O_abs = 2^(m + Gs) O_acc.
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   const bool has_o = m_run != -INFINITY && Gs != kGUnset;
   const float my_e = has_o ? m_run + (float)Gs : -INFINITY;
   if (stuck) s_err = 1;
-  if (half == 0 && grp == 0) {
-    s_m[pair][row] = m_run;
-    s_l[pair][row] = l_run;
-    s_e[pair][row] = my_e;
+  if (grp == 0) {
+    s_l[wave][row] = l_run;
+    if (half == 0) {
+      s_m[pair][row] = m_run;
+      s_e[pair][row] = my_e;
+    }
   }
-  __syncthreads();   // also: every wave is past its last K-row read
+  __syncthreads();   // also: every wave is past its last row read
   float E = -INFINITY;
 #pragma unroll
   for (int q = 0; q < kPairs; ++q) E = fmaxf(E, s_e[q][row]);
   {
-    const float f = my_e == -INFINITY ? 0.0f : __builtin_ldexpf(1.0f, max((int)(my_e - E), -200));
+    const float f = my_e == -INFINITY ? 0.0f : pow2i(my_e - E);
 #pragma unroll
     for (int q = 0; q < 16; ++q) o[q] *= f;
   }
@@ -526,7 +541,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     if (Mh != -INFINITY) {
 #pragma unroll
       for (int q = 0; q < kPairs; ++q)
-        if (s_m[q][hd] != -INFINITY) den += __builtin_amdgcn_exp2f(s_m[q][hd] - Mh) * s_l[q][hd];
+        if (s_m[q][hd] != -INFINITY)
+          den += __builtin_amdgcn_exp2f(s_m[q][hd] - Mh) * (s_l[2 * q][hd] + s_l[2 * q + 1][hd]);
     }
     if (splits == 1) {
       float sc = 0.0f;
