@@ -59,7 +59,6 @@ constexpr int kRowBytes = 16 * kLat * 2;          // fp16 latent rows of one pag
 constexpr int kStageRowU4 = (kLat + 64) / 8 + 1;  // bf16 Q staging row, uint4 units
 constexpr float kTau = 8.0f;                      // lazy-max slack, log2 units
 constexpr int kGUnset = -(1 << 20);               // Gs before any nonzero outer scale
-constexpr int kSlabRow = kHalf + 4;               // merge slab row (floats, padded)
 constexpr int kBtPerThread = 4;                   // block-table entries staged per thread
 constexpr int kMaxSplitPages = kBtPerThread * kThreads;   // pages of one split (2,048)
 constexpr int kBufs = 2;                          // pages of record bytes in flight per wave
@@ -73,7 +72,7 @@ constexpr int kQLds = 16 + 2 - kQReg;             // the other latent steps and 
 // LDS: the latent rows of each wave's page. Before the loop the region holds
 // the staged bf16 Q; after it, the merge slabs.
 constexpr int kRowsBytes = kWaves * kRowBytes;
-static_assert(2 * 2 * kHeads * kSlabRow * 4 <= kRowsBytes, "merge slabs fit");
+static_assert(kWaves * 16 * 64 * 16 <= kRowsBytes, "merge slabs fit");
 static_assert(((kHeads * (kLat + 64) / 8 + kThreads - 1) / kThreads * kThreads / ((kLat + 64) / 8) + 1) *
                   kStageRowU4 * 16 <= kRowsBytes,
               "staged Q, with the prologue's spill-over rows, fits");
@@ -123,6 +122,22 @@ __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shf
 // 2^e as fp32 for an integer-valued e (0 below 2^-200)
 __device__ __forceinline__ float pow2i(float e) { return __builtin_ldexpf(1.0f, max((int)e, -200)); }
 
+// Block i of a grid of batch * inner blocks -> (sequence b, inner index j).
+// Workgroups are dispatched to the 8 XCDs round robin (block i on XCD i % 8);
+// when batch is a multiple of 8 every block of sequence b lands on XCD b % 8,
+// so the split partials of a sequence stay in one XCD's L2 for the combine.
+__device__ __forceinline__ void xcd_local(int i, int batch, int inner, int &b, int &j) {
+  if ((batch & 7) == 0) {
+    const int nb = batch >> 3;
+    const int r = i >> 3;
+    b = (r % nb) * 8 + (i & 7);
+    j = r / nb;
+  } else {
+    b = i / inner;
+    j = i - b * inner;
+  }
+}
+
 // The record bytes of one page that a wave needs, in the MFMA layout (lane =
 // key `row`, dim group `grp`).
 struct PageOp {
@@ -155,8 +170,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   const int row = lane & 15;          // key of the A operand / head of the output
   const int grp = lane >> 4;
   // work item: (sequence b, split); the query is row b
-  const int b = blockIdx.x / splits;
-  const int split = blockIdx.x - b * splits;
+  int b, split;
+  xcd_local(blockIdx.x, a.batch, splits, b, split);
   const int qrow = b;
   const int p_begin = split * pages_per_split;
   const int32_t *bt = a.block_table + (size_t)b * a.bt_stride;
@@ -495,6 +510,9 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     }
   }
   __syncthreads();   // also: every wave is past its last row read
+  // a pair wait that gave up leaves NaN outputs (or NaN partials, which the
+  // combine turns into NaN outputs) rather than silently wrong values
+  const bool failed = s_err != 0;
   float E = -INFINITY;
 #pragma unroll
   for (int q = 0; q < kPairs; ++q) E = fmaxf(E, s_e[q][row]);
@@ -503,46 +521,35 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
 #pragma unroll
     for (int q = 0; q < 16; ++q) o[q] *= f;
   }
-  // pairs 2, 3 hand their halves to pairs 0, 1, which add them in place; the
-  // last add happens on the way out
-  float *slab = (float *)smem;   // [2 pair slots][2 halves][16 heads][kSlabRow]
-  auto slab_at = [&](int slot, int h, int hd, int d) -> float * {
-    return slab + ((size_t)(slot * 2 + h) * kHeads + hd) * kSlabRow + d;
-  };
-  if (pair >= 2) {
+  // every wave leaves its scaled half of O in LDS (tile-major, lane-minor:
+  // conflict-free 16-byte writes); the output pass adds the four pairs
+  v4f *slab = (v4f *)smem;   // [wave][16 tiles][64 lanes]
 #pragma unroll
-    for (int q = 0; q < 16; ++q) *(v4f *)slab_at(pair - 2, half, row, 16 * q + 4 * grp) = o[q];
-  }
+  for (int q = 0; q < 16; ++q) slab[(wave * 16 + q) * 64 + lane] = o[q];
   __syncthreads();
-  if (pair < 2) {
+  // output: per thread and pass one slab entry (half h, tile q, lane ln:
+  // dims 256h + 16q + 4(ln/16) .. +4 of head ln%16); consecutive threads read
+  // consecutive entries, so the four pair reads are conflict-free
+  for (int e = threadIdx.x; e < 2 * 16 * 64; e += kThreads) {
+    const int h = e >> 10;
+    const int q = (e >> 6) & 15;
+    const int ln = e & 63;
+    const int hd = ln & 15;
+    const int d = kHalf * h + 16 * q + 4 * (ln >> 4);
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      v4f *dst = (v4f *)slab_at(pair, half, row, 16 * q + 4 * grp);
-      *dst = o[q] + *dst;
-    }
-  }
-  __syncthreads();
-  // a pair wait that gave up leaves NaN outputs (or NaN partials, which the
-  // combine turns into NaN outputs) rather than silently wrong values
-  const bool failed = s_err != 0;
-  // output: 4 consecutive dims per thread and pass
-  for (int e4 = threadIdx.x; e4 < kHeads * kLat / 4; e4 += kThreads) {
-    const int hd = e4 / (kLat / 4);
-    const int d = 4 * (e4 - hd * (kLat / 4));
-    const int h = d / kHalf;
-    const int dd = d - h * kHalf;
-    const v4f acc = *(const v4f *)slab_at(0, h, hd, dd) + *(const v4f *)slab_at(1, h, hd, dd);
+    for (int pr = 0; pr < kPairs; ++pr) acc += slab[((2 * pr + h) * 16 + q) * 64 + ln];
     float Mh = -INFINITY, Eh = -INFINITY, den = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kPairs; ++q) {
-      Mh = fmaxf(Mh, s_m[q][hd]);
-      Eh = fmaxf(Eh, s_e[q][hd]);
+    for (int pr = 0; pr < kPairs; ++pr) {
+      Mh = fmaxf(Mh, s_m[pr][hd]);
+      Eh = fmaxf(Eh, s_e[pr][hd]);
     }
     if (Mh != -INFINITY) {
 #pragma unroll
-      for (int q = 0; q < kPairs; ++q)
-        if (s_m[q][hd] != -INFINITY)
-          den += __builtin_amdgcn_exp2f(s_m[q][hd] - Mh) * (s_l[2 * q][hd] + s_l[2 * q + 1][hd]);
+      for (int pr = 0; pr < kPairs; ++pr)
+        if (s_m[pr][hd] != -INFINITY)
+          den += __builtin_amdgcn_exp2f(s_m[pr][hd] - Mh) * (s_l[2 * pr][hd] + s_l[2 * pr + 1][hd]);
     }
     if (splits == 1) {
       float sc = 0.0f;
@@ -567,10 +574,12 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
 constexpr int kCombineThreads = kLat / 4;
 constexpr int kMaxCombineSplits = 64;
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const float *part_o, const float *part_ml,
-                                                                      uint16_t *out, int splits) {
+                                                                      uint16_t *out, int batch, int splits) {
   __shared__ float s_w[2][kMaxCombineSplits];   // per split: O weight, denominator weight
   __shared__ float s_f;                          // 2^(E - M) / den, or 0
-  const int bh = blockIdx.x;
+  int b, h;
+  xcd_local(blockIdx.x, batch, kHeads, b, h);    // on the XCD that wrote sequence b's partials
+  const int bh = b * kHeads + h;
   const int t = threadIdx.x;
   const float *ml = part_ml + (size_t)bh * splits * 4;
   const float *po = part_o + (size_t)bh * splits * kLat + 4 * t;
@@ -624,7 +633,7 @@ hipError_t launch_decode_mla(const DecodeMlaLaunch &a, const MlaPlan &p, hipStre
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((size_t)a.batch * a.hq)), dim3(kCombineThreads), 0, s,
-                     a.part_o, a.part_ml, a.out, p.splits);
+                     a.part_o, a.part_ml, a.out, a.batch, p.splits);
   return hipGetLastError();
 }
 
