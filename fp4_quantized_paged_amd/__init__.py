@@ -49,10 +49,11 @@ class AttnParams(ctypes.Structure):
                 ("flags", ctypes.c_uint32)]
 
 FLAG_PREFILL_FP8_P = 1
+FLAG_PREFILL_FP8_P2 = 2
 
 
 _lib = None
-ABI_VERSION = 5   # KVQ_ABI_VERSION of include/kvq.h
+ABI_VERSION = 6   # KVQ_ABI_VERSION of include/kvq.h
 
 _SIGNATURES = {
     "kvq_abi_version": (ctypes.c_int, []),
@@ -401,10 +402,11 @@ def prefill(cache, q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,
             softmax_scale: float, q_scale: float = 1.0, k_scale: float = 1.0,
             v_scale: float = 1.0, window: int = 0, slopes: Optional[torch.Tensor] = None,
             out: Optional[torch.Tensor] = None, rel_bias: Optional[torch.Tensor] = None,
-            fp8_p: bool = False) -> torch.Tensor:
+            fp8_p: bool = False, fp8_p2: bool = False) -> torch.Tensor:
     """kvq_paged_attn_prefill. q bf16 [sumQ, Hq, Dqk] -> out bf16 [sumQ, Hq, Dv].
     rel_bias: learned relative-bias table, bf16 [Hq, extent]. fp8_p: the
-    single-term e4m3 P speed variant (KVQ_FLAG_PREFILL_FP8_P)."""
+    single-term e4m3 P speed variant (KVQ_FLAG_PREFILL_FP8_P); fp8_p2: the
+    two-term e4m3 P path (KVQ_FLAG_PREFILL_FP8_P2)."""
     _need_cuda(q, cu_q_lens, block_table, seq_lens, slopes, rel_bias, out)
     dqk, dv = _head_dims(cache)
     if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous() or q.shape[2] != dqk:
@@ -422,7 +424,7 @@ def prefill(cache, q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,
         out = torch.empty((total_q, Hq, dv), dtype=torch.bfloat16, device=q.device)
     _check_out(out, (total_q, Hq, dv))
     p = _params(Hq, softmax_scale, q_scale, k_scale, v_scale, window, slopes, 0, rel_bias,
-                FLAG_PREFILL_FP8_P if fp8_p else 0)
+                (FLAG_PREFILL_FP8_P if fp8_p else 0) | (FLAG_PREFILL_FP8_P2 if fp8_p2 else 0))
     st = lib().kvq_paged_attn_prefill(ctypes.byref(d), _ptr(q), _ptr(cu_q_lens), total_q,
                                       int(max_q_len), _ptr(block_table), block_table.stride(0),
                                       _ptr(seq_lens), int(seq_lens.shape[0]), int(max_seq_len),

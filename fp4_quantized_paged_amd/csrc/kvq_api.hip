@@ -51,7 +51,9 @@ int check_cache(const kvq_cache *c) {
 int check_params(const kvq_cache *c, const kvq_attn_params *p) {
   if (p == nullptr) return KVQ_ERR_INVALID_ARG;
   if (p->num_q_heads <= 0 || p->num_q_heads % c->num_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
-  if (p->window < 0 || p->num_splits < 0 || (p->flags & ~static_cast<uint32_t>(KVQ_FLAG_PREFILL_FP8_P)) != 0)
+  const uint32_t known = KVQ_FLAG_PREFILL_FP8_P | KVQ_FLAG_PREFILL_FP8_P2;
+  if (p->window < 0 || p->num_splits < 0 || (p->flags & ~known) != 0 ||
+      (p->flags & known) == known)
     return KVQ_ERR_INVALID_ARG;
   if (p->rel_bias != nullptr) {
     if (p->rel_extent < 1 || p->rel_extent > (1 << 20) || p->alibi_slopes != nullptr ||
@@ -451,7 +453,7 @@ int kvq_paged_attn_prefill(const kvq_cache *cache, const void *q, const int32_t 
   a.d = cache->head_dim;
   a.window = params->window;
   a.max_q_len = max_q_len;
-  a.fp8_p = (params->flags & KVQ_FLAG_PREFILL_FP8_P) != 0;
+  a.p_mode = (params->flags & KVQ_FLAG_PREFILL_FP8_P) != 0 ? 1 : ((params->flags & KVQ_FLAG_PREFILL_FP8_P2) != 0 ? 2 : 0);
   a.q_inv = 1.0f / params->q_scale;
   a.fold_log2 = params->softmax_scale * params->q_scale * params->k_scale * 1.4426950408889634f;
   a.v_scale = params->v_scale;

@@ -95,7 +95,8 @@ struct PrefillE4M3Launch {
   int rel_extent;
   uint16_t *out;
   int batch, hq, hkv, d, window, max_q_len;
-  int fp8_p;                   // single-term e4m3 P with lazy rescale (opt-in variant)
+  int p_mode;                  // P of PV: 0 bf16; 1 one e4m3 term, 2 two e4m3 terms (both
+                               // with a lazy rescale of slack 0.75, on fp8 MFMA)
   float q_inv, fold_log2, v_scale;
 };
 hipError_t launch_prefill_e4m3(const PrefillE4M3Launch &a, hipStream_t s);

@@ -121,9 +121,13 @@ constexpr float kLazySlack = 0.75f;
 constexpr float kLazyBf16 = 8.0f;
 constexpr float kZeroGap = 160.0f;
 
-template <int kKind, bool kP8>
+// P representations of PV: bf16 (default), one e4m3 term, two e4m3 terms.
+constexpr int kPBf16 = 0, kPFp8 = 1, kPFp8x2 = 2;
+
+template <int kKind, int kPMode>
 __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blocks, int chunk, int nchunks) {
+  constexpr bool kP8 = kPMode != kPBf16;
   __shared__ PrefillSmem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -356,7 +360,8 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
       s[1][j] = mfma_16x16x128_e4m3(kop, qop[1], v4f{0.f, 0.f, 0.f, 0.f});
     }
     uint4 pk[2][4];     // P in bf16: pk[cb][kk] holds keys 8kk .. 8kk+7 of the lane group
-    v8i pk8[2];         // fp8-P variant: byte 4j + i of pk8[cb] is key 32*grp + 4j + i
+    v8i pk8[2];         // fp8-P variants: byte 4j + i of pk8[cb] is key 32*grp + 4j + i
+    v8i pk8l[2];        // two-term variant: the second term, same layout
     const float scale = kBias ? 1.0f : fold;
     float xmax[2];      // the block's largest exponent argument of this lane's query row
 #pragma unroll
@@ -417,7 +422,15 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
           float pv[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(s[cb][j][i], scale, off8));
-          pk8[cb][j] = (int)cvt4_e4m3(pv[0], pv[1], pv[2], pv[3]);
+          const uint32_t hi = cvt4_e4m3(pv[0], pv[1], pv[2], pv[3]);
+          pk8[cb][j] = (int)hi;
+          if constexpr (kPMode == kPFp8x2) {
+            // second term: e4m3 of what the first one left (exact difference
+            // in fp32), so each weight keeps about 8 significant bits
+            const v2f h01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+            const v2f h23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+            pk8l[cb][j] = (int)cvt4_e4m3(pv[0] - h01.x, pv[1] - h01.y, pv[2] - h23.x, pv[3] - h23.y);
+          }
         }
         if (__ballot(alpha != 1.0f)) {
 #pragma unroll
@@ -462,14 +475,22 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
         const v8i va = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         o[0][t] = mfma_16x16x128_e4m3(va, pk8[0], o[0][t]);
         o[1][t] = mfma_16x16x128_e4m3(va, pk8[1], o[1][t]);
+        if constexpr (kPMode == kPFp8x2) {
+          o[0][t] = mfma_16x16x128_e4m3(va, pk8l[0], o[0][t]);
+          o[1][t] = mfma_16x16x128_e4m3(va, pk8l[1], o[1][t]);
+        }
       }
       ol[0] = mfma_16x16x128_e4m3(ones8, pk8[0], ol[0]);
       ol[1] = mfma_16x16x128_e4m3(ones8, pk8[1], ol[1]);
-      // operands just in time (two LDS reads, then their two MFMAs)
+      if constexpr (kPMode == kPFp8x2) {
+        ol[0] = mfma_16x16x128_e4m3(ones8, pk8l[0], ol[0]);
+        ol[1] = mfma_16x16x128_e4m3(ones8, pk8l[1], ol[1]);
+      }
+      // operands just in time (two LDS reads, then their MFMAs)
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kPMode == kPFp8x2 ? 4 : 2, 0);
       }
       continue;
     }
@@ -524,15 +545,19 @@ hipError_t launch_prefill_e4m3(const PrefillE4M3Launch &a, hipStream_t s) {
   const size_t grid = (size_t)8 * (((size_t)units * nchunks + 7) / 8) * chunk;
   const dim3 g((unsigned)grid), b(64 * kPW);
   const int kind = a.slopes != nullptr ? kBiasSlope : (a.rel != nullptr ? kBiasTable : kBiasNone);
-  if (a.fp8_p) {
-    if (kind == kBiasSlope) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasSlope, true>), g, b, 0, s, a, tiles, units, head_blocks, chunk, nchunks);
-    else if (kind == kBiasTable) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasTable, true>), g, b, 0, s, a, tiles, units, head_blocks, chunk, nchunks);
-    else hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasNone, true>), g, b, 0, s, a, tiles, units, head_blocks, chunk, nchunks);
-  } else {
-    if (kind == kBiasSlope) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasSlope, false>), g, b, 0, s, a, tiles, units, head_blocks, chunk, nchunks);
-    else if (kind == kBiasTable) hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasTable, false>), g, b, 0, s, a, tiles, units, head_blocks, chunk, nchunks);
-    else hipLaunchKernelGGL((prefill_e4m3_kernel<kBiasNone, false>), g, b, 0, s, a, tiles, units, head_blocks, chunk, nchunks);
-  }
+#define KVQ_PREFILL_LAUNCH(K, P) \
+  hipLaunchKernelGGL((prefill_e4m3_kernel<K, P>), g, b, 0, s, a, tiles, units, head_blocks, chunk, nchunks)
+#define KVQ_PREFILL_KINDS(P)                                   \
+  do {                                                         \
+    if (kind == kBiasSlope) KVQ_PREFILL_LAUNCH(kBiasSlope, P); \
+    else if (kind == kBiasTable) KVQ_PREFILL_LAUNCH(kBiasTable, P); \
+    else KVQ_PREFILL_LAUNCH(kBiasNone, P);                      \
+  } while (0)
+  if (a.p_mode == 1) KVQ_PREFILL_KINDS(kPFp8);
+  else if (a.p_mode == 2) KVQ_PREFILL_KINDS(kPFp8x2);
+  else KVQ_PREFILL_KINDS(kPBf16);
+#undef KVQ_PREFILL_KINDS
+#undef KVQ_PREFILL_LAUNCH
   return hipGetLastError();
 }
 

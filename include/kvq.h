@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 5
+#define KVQ_ABI_VERSION 6
 
 /* A hipStream_t. NULL selects the null stream. */
 typedef struct ihipStream_t *kvq_stream_t;
@@ -136,7 +136,16 @@ enum {
      "Tier 0"). A speed variant: its error is within the pages' fp8 test
      tolerance (atol and rtol 0.15, [PR54705] "Test Plan"), not within this
      library's default attention tolerance, so it is off unless requested. */
-  KVQ_FLAG_PREFILL_FP8_P = 1u
+  KVQ_FLAG_PREFILL_FP8_P = 1u,
+  /* Prefill only: P = 2^8 p as two e4m3 terms (hi = e4m3(P), lo = e4m3(P -
+     hi)) on fp8 MFMA, with the same lazy running max (slack 0.75) and a
+     normaliser summed from the same two terms ([PR54705] evidence "Tier 0"
+     for the 2^8 pre-scale and its log2(448) - 8 bound). About 8 significant
+     bits per weight, like the default bf16 P; an alternative P path kept for
+     its measured comparison with the default (two fp8 MFMAs cost what one
+     bf16 MFMA does, and the split costs vector instructions). At most one of
+     the two flags may be set. */
+  KVQ_FLAG_PREFILL_FP8_P2 = 2u
 };
 
 /*

@@ -127,7 +127,9 @@ def test_decode_validation(lib):
     assert decode(lib, d, params(rel_bias=FAKE + 1, rel_extent=128)) == -1   # misaligned bf16
     assert decode(lib, d, params(rel_bias=FAKE, rel_extent=128, alibi_slopes=FAKE)) == -1
     assert decode(lib, d, params(rel_bias=FAKE, rel_extent=128), B=0) == 0
-    assert decode(lib, d, params(flags=2)) == -1                     # unknown flag bit
+    assert decode(lib, d, params(flags=4)) == -1                     # unknown flag bit
+    assert decode(lib, d, params(flags=3)) == -1                     # both P variants at once
+    assert decode(lib, d, params(flags=2), B=0) == 0                 # the two-term prefill flag
     assert decode(lib, d, params(flags=1), B=0) == 0                 # the prefill flag: ignored here
     for bad in (0.0, -2.0, math.nan, math.inf):
         assert decode(lib, d, params(softmax_scale=bad)) == -3

@@ -137,6 +137,32 @@ def test_prefill_fp8_p_variant(lens, qlens, hq, hkv, window, bias):
     assert torch.equal(again, out)
 
 
+@pytest.mark.parametrize("lens,qlens,hq,hkv,window,bias", FP8P_CASES)
+def test_prefill_fp8_p2_variant(lens, qlens, hq, hkv, window, bias):
+    """Two e4m3 terms of P on fp8 MFMA: the default tolerance applies."""
+    kw = {}
+    if bias == "slopes":
+        kw["slopes"] = geometric_slopes(hq)
+    elif bias is not None:
+        kw["rel_extent"] = bias
+    c = make_attn_case("prefill_p82", 600 + sum(qlens) + hq, lens, qlens, hq, hkv, 128,
+                       v_std=2.0, window=window, **kw)
+    dc, out, ref = run_case(c, fp8_p2=True)
+    print(check_attention(out, ref, "fp8 P x2 %s %s w%d %s" % (lens, qlens, window, bias)))
+
+
+def test_chunked_prefill_fp8_p2_full_size_sampled():
+    c = config_chunked_prefill()
+    rng = np.random.default_rng(2)
+    rows = []
+    for b in (0, 2):
+        r0 = int(c.cu_q_lens[b])
+        picks = np.concatenate([[0, 2047], rng.choice(2048, 30, replace=False)])
+        rows += list(r0 + np.unique(picks))
+    _, out, ref = run_case(c, rows=rows, seqs=[0, 2], fp8_p2=True)
+    print(check_attention(out, ref, "chunked_prefill fp8 P x2"))
+
+
 def test_chunked_prefill_fp8_p_full_size_sampled():
     c = config_chunked_prefill()
     rng = np.random.default_rng(1)
@@ -156,9 +182,9 @@ def slope_table(slopes, extent):
     return torch.from_numpy(prod).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("fp8_p", [False, True])
+@pytest.mark.parametrize("pmode", ["bf16", "fp8_p", "fp8_p2"])
 @pytest.mark.parametrize("which", ["small", "full"])
-def test_prefill_slope_early_stop_is_exact(which, fp8_p):
+def test_prefill_slope_early_stop_is_exact(which, pmode):
     """With the slope bias a wave stops once a bound puts every remaining
     probability at exactly zero, and both bias kinds skip blocks whose every P
     is zero. The learned-table path, given a table holding the same bf16
@@ -173,11 +199,12 @@ def test_prefill_slope_early_stop_is_exact(which, fp8_p):
     dc = DeviceCase(c)
     s = dc.calibrate()
     dc.store_all(s)
-    a = dc.prefill(s, fp8_p=fp8_p)
+    mode = {} if pmode == "bf16" else {pmode: True}
+    a = dc.prefill(s, **mode)
     tab = slope_table(c.slopes, c.max_seq_len).cuda()
     b = kvq.prefill(dc.cache, dc.q, dc.cu_q_lens, c.max_q_len, dc.block_table, dc.seq_lens,
                     c.max_seq_len, c.softmax_scale, s["q"], s["k"], s["v"], c.window, None,
-                    rel_bias=tab, fp8_p=fp8_p)
+                    rel_bias=tab, **mode)
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(a.float()))
     assert torch.equal(a, b)
