@@ -9,12 +9,19 @@ Scales come from amax calibration over the resident inputs before timing.
 ``value`` is the step's algorithmic HBM bytes divided by the step time (GB/s).
 The JSON line also carries the roofline of the dominant kernel (decode attention,
 timed with HIP events on the launch stream), the other rows of the path measured
-in the same run (bulk store tokens/s, calibration, long-context decode, chunked
-prefill, NVFP4 record store and MLA decode), and the CPU oracle timed on a
-bounded sample as a baseline.
+in the same run (stores, calibration, long-context and single-stream decode,
+chunked and sliding-window prefill, NVFP4 record store, MLA decode and prefill),
+and the CPU oracle timed on a bounded sample as a baseline.
+
+Every row is timed the same way: 5 warm-up calls, then 20 groups of a few
+back-to-back calls, each group between one pair of HIP events on the launch
+stream; a row reports the median and the minimum of the per-call times over
+the groups, a roofline object (algorithmic bytes or flops per call over the
+median time, against the MI355X peak of the unit that bounds it) and the
+SHA-256 of its inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-extras]
-       [--skip-cpu] [--only-decode] [--copy-probe]
+       [--skip-cpu] [--only ROW] [--copy-probe]
 """
 from __future__ import annotations
 
@@ -31,6 +38,11 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 FP8_PEAK_TFLOPS = 5000.0        # dense fp8 MFMA
 FP16_PEAK_TFLOPS = 2500.0       # dense fp16 / bf16 MFMA
 BF16_PEAK_TFLOPS = 2500.0
+# e4m3 prefill: QK^T on fp8 MFMA and PV on bf16 MFMA, half the flops each:
+# the time at peak is F/2 / 5000 + F/2 / 2500, i.e. a mixed peak of 3333 TFLOP/s
+PREFILL_MIXED_PEAK_TFLOPS = 1.0 / (0.5 / FP8_PEAK_TFLOPS + 0.5 / BF16_PEAK_TFLOPS)
+REPS = 20            # timed groups per row
+WARM = 5             # warm-up calls per row
 
 
 def parse():
@@ -42,8 +54,9 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true", help="no CPU oracle baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a 1 GiB device copy (HBM counter calibration)")
-    ap.add_argument("--only", choices=["prefill", "long_context", "nvfp4", "nvfp4_prefill"], default=None,
-                    help="run only this row (for profiling); prints its JSON")
+    ap.add_argument("--only", choices=["prefill", "long_context", "nvfp4", "nvfp4_prefill", "tier1", "stores",
+                                       "mla_decode"], default=None,
+                    help="run only these rows (for profiling); prints their JSON")
     return ap.parse_args()
 
 
@@ -175,7 +188,8 @@ def main():
     torch.cuda.set_device(0)
     if args.only is not None:
         fn = {"prefill": prefill_rows, "long_context": long_context_rows, "nvfp4": nvfp4_rows,
-              "nvfp4_prefill": nvfp4_prefill_rows}[args.only]
+              "nvfp4_prefill": nvfp4_prefill_rows, "tier1": tier1_rows, "stores": write_path_rows,
+              "mla_decode": mla_decode_only}[args.only]
         print(json.dumps(fn(torch, kvq)), flush=True)
         return
     dev = "cuda"
@@ -183,6 +197,7 @@ def main():
     # ---------------- headline: batched decode step ----------------
     log("generating batched-decode inputs")
     c = config_batched_decode()
+    sha = case_sha(c)
     B, Hq, Hkv, D, L = c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim, c.max_seq_len
     k = c.k.to(dev)
     v = c.v.to(dev)
@@ -261,6 +276,7 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_record(),
                      "bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_ms * 1e3, 2)},
+        "inputs_sha256": sha,
         "step_unfused_us": round(unfused_ms * 1e3, 2),
     }
     log("decode %.2f us, %.0f GB/s (%.1f%% of peak)" % (dec_ms * 1e3, achieved,
@@ -274,16 +290,14 @@ def main():
         def decode_rel(i):
             kvq.decode(caches[i % 2], q, bt, seq_lens, L, c.softmax_scale, scales["q"], scales["k"],
                        scales["v"], out=out, workspace=ws, rel_bias=rel)
-        for i in range(2):
-            decode_rel(i)
-        rms = back_to_back_ms(torch, decode_rel, args.steps)
-        rel_rows["decode_rel1024"] = {"us": round(rms * 1e3, 2),
-                                      "GB_s": round(dec_bytes / (rms * 1e-3) / 1e9, 1),
-                                      "pct_of_peak": round(100 * dec_bytes / (rms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+        rel_rows["decode_rel1024"] = timed_row(torch, decode_rel, "hbm", dec_bytes, HBM_PEAK_GBPS, "GB/s",
+                                               per=5, sha=sha)
+        rel_rows["decode"] = timed_row(torch, decode, "hbm", dec_bytes, HBM_PEAK_GBPS, "GB/s", per=5, sha=sha,
+                                       roof_extra={"kernel": "decode_e4m3_kernel"})
     del caches, k_new, v_new
 
     if not args.skip_extras:
-        result["rows"] = extras(torch, kvq, c, k, v, q, slot, scales)
+        result["rows"] = extras(torch, kvq, c, k, v, q, slot, scales, sha)
         result["rows"].update(rel_rows)
     del k, v, q
     torch.cuda.empty_cache()
@@ -310,58 +324,132 @@ def back_to_back_ms(torch, fn, reps):
     return t.mean_ms() / reps
 
 
-def timed_mean(torch, fn, reps=10, warm=2):
-    """Mean GPU time of fn() over reps back-to-back calls after warm calls."""
-    for _ in range(warm):
-        fn()
-    return back_to_back_ms(torch, lambda i: fn(), reps)
+def timed_stats(torch, fn, per=5, reps=REPS, warm=WARM):
+    """Per-call GPU time of fn(i) in microseconds: WARM warm-up calls, then
+    REPS groups of `per` back-to-back calls, each group between one pair of
+    HIP events. Returns (median, min) over the groups. The call index i keeps
+    counting across groups, so callers that alternate buffers by i do."""
+    for i in range(warm):
+        fn(i)
+    base = [warm]
+    samples = []
+    for _ in range(reps):
+        off = base[0]
+        samples.append(back_to_back_ms(torch, lambda j: fn(off + j), per) * 1e3)
+        base[0] += per
+    return float(np.median(samples)), float(np.min(samples))
 
 
-def extras(torch, kvq, c, k, v, q, slot, scales):
-    """Other rows of the path, each timed with HIP events (mean of reps)."""
+def roofline(bound, amount, us, peak, unit, **extra):
+    """Roofline record of one call: `amount` algorithmic bytes (unit GB/s) or
+    flops (TFLOP/s) over `us` microseconds against `peak`."""
+    scale = 1e9 if unit == "GB/s" else 1e12
+    achieved = amount / (us * 1e-6) / scale
+    rec = {"bound": bound, "achieved": round(achieved, 1), "peak": round(peak, 1), "unit": unit,
+           "frac": round(achieved / peak, 4), ("bytes" if unit == "GB/s" else "flops"): int(amount)}
+    rec.update(extra)
+    return rec
+
+
+def timed_row(torch, fn, bound, amount, peak, unit, per=5, sha=None, roof_extra=None, **fields):
+    """One bench row: median / min per-call time and the roofline at the median."""
+    med, mn = timed_stats(torch, fn, per=per)
+    row = dict(fields)
+    row.update({"us_median": round(med, 2), "us_min": round(mn, 2), "reps": REPS, "calls_per_rep": per,
+                "roofline": roofline(bound, amount, med, peak, unit, **(roof_extra or {}))})
+    if sha is not None:
+        row["inputs_sha256"] = sha
+    return row
+
+
+def sha256_of(*arrays):
+    """SHA-256 over the bytes of the given host arrays / CPU tensors, in order."""
+    import hashlib
+    import torch
+    h = hashlib.sha256()
+    for a in arrays:
+        if a is None:
+            continue
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().contiguous().reshape(-1).view(torch.uint8).numpy()
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
+
+
+def case_sha(c):
+    """SHA-256 of an attention workload's inputs (Q, K, V, slots, block table,
+    lengths, new-token counts, slopes or bias table)."""
+    return sha256_of(c.q, c.k, c.v, c.slot_mapping, c.block_table, c.seq_lens, c.cu_q_lens, c.slopes, c.rel)
+
+
+def mla_sha(c):
+    return sha256_of(c.q, c.kv, c.slot_mapping, c.block_table, c.seq_lens)
+
+
+def extras(torch, kvq, c, k, v, q, slot, scales, sha):
+    """Other rows of the path on the batched-decode inputs, then the other
+    workloads' rows."""
     rows = {}
     Hkv, D = c.num_kv_heads, c.head_dim
     T = k.shape[0]
-    # bulk quant-on-store of all 524,288 tokens
+    # bulk quant-on-store of all 524,288 tokens (1 GiB of bf16 read per call)
     cache = kvq.E4M3Cache(c.num_pages, Hkv, D)
-    ms = timed_mean(torch, lambda: kvq.store(cache, k, v, slot, scales["k"], scales["v"]))
     sb = store_bytes(T, Hkv, D)
-    rows["store_bulk"] = {"tokens": T, "us": round(ms * 1e3, 2),
-                          "tokens_per_s": round(T / (ms * 1e-3), 1),
-                          "GB_s": round(sb / (ms * 1e-3) / 1e9, 1),
-                          "pct_of_peak": round(100 * sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
-    # decode append: the 64 new tokens only
+    rows["store_bulk"] = timed_row(torch, lambda i: kvq.store(cache, k, v, slot, scales["k"], scales["v"]),
+                                   "hbm", sb, HBM_PEAK_GBPS, "GB/s", per=2, sha=sha, tokens=T,
+                                   kv_heads=Hkv)
+    rows["store_bulk"]["tokens_per_s"] = round(T / (rows["store_bulk"]["us_median"] * 1e-6), 1)
+    # decode append: the 64 new tokens only (latency-bound)
     idx = torch.from_numpy(np.cumsum(c.seq_lens) - 1).to(k.device)
     kn, vn, sn = k[idx].contiguous(), v[idx].contiguous(), slot[idx].contiguous()
-    ms = timed_mean(torch, lambda: kvq.store(cache, kn, vn, sn, scales["k"], scales["v"]), reps=20)
-    rows["store_append"] = {"tokens": int(kn.shape[0]), "us": round(ms * 1e3, 2)}
-    # the store sizes of the write-path benchmark on the vLLM PR 54705 page
-    # ("Tier 1"): 33, 2,048 and 16,384 tokens, the workload's first tokens
-    sweep = {}
-    for n in (33, 2048, 16384):
-        kn_, vn_, sn_ = k[:n].contiguous(), v[:n].contiguous(), slot[:n].contiguous()
-        ms = timed_mean(torch, lambda: kvq.store(cache, kn_, vn_, sn_, scales["k"], scales["v"]), reps=20)
-        sweep[str(n)] = {"us": round(ms * 1e3, 2), "tokens_per_s": round(n / (ms * 1e-3), 1),
-                         "GB_s": round(store_bytes(n, Hkv, D) / (ms * 1e-3) / 1e9, 1)}
-    rows["store_sweep"] = sweep
-    # calibration over K and V
+    rows["store_append"] = timed_row(torch, lambda i: kvq.store(cache, kn, vn, sn, scales["k"], scales["v"]),
+                                     "hbm", store_bytes(64, Hkv, D), HBM_PEAK_GBPS, "GB/s", per=10, sha=sha,
+                                     tokens=int(kn.shape[0]), note="latency-bound")
+    # calibration over K and V (2 bytes read per element)
     amax = torch.zeros(1, device=k.device)
-    ms = timed_mean(torch, lambda: (kvq.calibrate_amax(k, amax=amax), kvq.calibrate_amax(v, amax=amax)))
     cb = 2 * k.numel() * 2
-    rows["calibrate_kv"] = {"us": round(ms * 1e3, 2), "GB_s": round(cb / (ms * 1e-3) / 1e9, 1)}
+    rows["calibrate_kv"] = timed_row(torch, lambda i: (kvq.calibrate_amax(k, amax=amax),
+                                                       kvq.calibrate_amax(v, amax=amax)),
+                                     "hbm", cb, HBM_PEAK_GBPS, "GB/s", per=2, sha=sha)
     # clip / flush-to-zero band counters of K and V at their scales
     counts = torch.zeros(2, dtype=torch.int64, device=k.device)
-    ms = timed_mean(torch, lambda: (kvq.band_counts(k, scales["k"], counts=counts),
-                                    kvq.band_counts(v, scales["v"], counts=counts)))
-    rows["band_counts_kv"] = {"us": round(ms * 1e3, 2), "GB_s": round(cb / (ms * 1e-3) / 1e9, 1),
-                              "pct_of_peak": round(100 * cb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+    rows["band_counts_kv"] = timed_row(torch, lambda i: (kvq.band_counts(k, scales["k"], counts=counts),
+                                                         kvq.band_counts(v, scales["v"], counts=counts)),
+                                       "hbm", cb, HBM_PEAK_GBPS, "GB/s", per=2, sha=sha)
     del cache
     torch.cuda.empty_cache()
+    rows.update(write_path_rows(torch, kvq))
     rows.update(tiny_decode_rows(torch, kvq))
     rows.update(long_context_rows(torch, kvq))
+    rows.update(tier1_rows(torch, kvq))
     rows.update(prefill_rows(torch, kvq))
     rows.update(nvfp4_rows(torch, kvq))
     return rows
+
+
+def write_path_rows(torch, kvq):
+    """The write path of the vLLM PR 54705 evidence document ("Tier 1": 2 head
+    configurations x {sliding, global} x {33, 2,048, 16,384} tokens). The
+    pages' model has 8 KV heads of 128 dims, 2 per rank at TP4: rows at 2, 4
+    (the batched-decode shape) and 8 KV heads. A sliding-window layer stores
+    its tokens with the same call as a global one (the window only decides
+    which pages a caller keeps), so one row covers both."""
+    from workloads import write_path_tokens
+    log("write path")
+    out = {}
+    dev = "cuda"
+    for hkv in (2, 4, 8):
+        for n in (33, 2048, 16384):
+            k, v, slot, num_pages = write_path_tokens(900 + hkv + n % 97, n, hkv)
+            sha = sha256_of(k, v, slot)
+            kd, vd, sd = k.to(dev), v.to(dev), torch.from_numpy(slot).to(dev)
+            cache = kvq.E4M3Cache(num_pages, hkv, 128)
+            r = timed_row(torch, lambda i: kvq.store(cache, kd, vd, sd, 0.05, 3.0), "hbm",
+                          store_bytes(n, hkv, 128), HBM_PEAK_GBPS, "GB/s", per=10, sha=sha,
+                          tokens=n, kv_heads=hkv)
+            r["tokens_per_s"] = round(n / (r["us_median"] * 1e-6), 1)
+            out["store_h%d_t%d" % (hkv, n)] = r
+    return out
 
 
 def tiny_decode_rows(torch, kvq):
@@ -376,11 +464,11 @@ def tiny_decode_rows(torch, kvq):
     bt = torch.from_numpy(c.block_table).to(dev)
     sl = torch.from_numpy(c.seq_lens).to(dev)
     out = torch.empty((c.batch, c.num_q_heads, c.head_dim), dtype=torch.bfloat16, device=dev)
-    ms = timed_mean(torch, lambda: kvq.decode(cache, q, bt, sl, c.max_seq_len, c.softmax_scale, 1.0, 1.0, 1.0,
-                                              out=out), reps=20)
     by = decode_bytes(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim, c.max_seq_len)
-    return {"tiny_decode": {"batch": c.batch, "context": c.max_seq_len, "us": round(ms * 1e3, 2),
-                            "bytes": by}}
+    return {"tiny_decode": timed_row(torch, lambda i: kvq.decode(cache, q, bt, sl, c.max_seq_len, c.softmax_scale,
+                                                                 1.0, 1.0, 1.0, out=out),
+                                     "hbm", by, HBM_PEAK_GBPS, "GB/s", per=10, sha=case_sha(c),
+                                     batch=c.batch, context=c.max_seq_len, note="latency-bound")}
 
 
 def nvfp4_rows(torch, kvq):
@@ -391,39 +479,34 @@ def nvfp4_rows(torch, kvq):
     from workloads import config_nvfp4_mla
     log("nvfp4 mla")
     c = config_nvfp4_mla(layer=0)
+    sha = mla_sha(c)
     dev = "cuda"
     kv = c.kv.to(dev)
     slot = torch.from_numpy(c.slot_mapping).to(dev)
     caches = [kvq.Nvfp4Cache(c.num_pages) for _ in range(2)]
-    ms_store = timed_mean(torch, lambda: kvq.store(caches[0], kv, None, slot, c.rope_scale), reps=5)
-    kvq.store(caches[1], kv, None, slot, c.rope_scale)
     T = int(kv.shape[0])
+    sb = T * (576 * 2 + 368 + 8)
+    rows = {}
+    rows["nvfp4_store"] = timed_row(torch, lambda i: kvq.store(caches[i % 2], kv, None, slot, c.rope_scale),
+                                    "hbm", sb, HBM_PEAK_GBPS, "GB/s", per=2, sha=sha, tokens=T)
+    rows["nvfp4_store"]["tokens_per_s"] = round(T / (rows["nvfp4_store"]["us_median"] * 1e-6), 1)
     del kv
     q = c.q.to(dev)
     bt = torch.from_numpy(c.block_table).to(dev)
     sl = torch.from_numpy(c.seq_lens).to(dev)
     out = torch.empty((c.batch, c.num_q_heads, 512), dtype=torch.bfloat16, device=dev)
-    it = [0]
-
-    def run():
-        cache = caches[it[0] % 2]     # 2 x 193 MB alternate: more than the Infinity Cache
-        it[0] += 1
-        kvq.decode(cache, q, bt, sl, c.max_seq_len, c.softmax_scale, k_scale=c.rope_scale, out=out)
-    ms = timed_mean(torch, run, reps=10)
     L = c.max_seq_len
+    ws = torch.zeros(max(kvq.decode_workspace_bytes(caches[0], c.batch, L, 16), 1), dtype=torch.uint8, device=dev)
     by = c.batch * (L * 368 + c.num_q_heads * (576 + 512) * 2 + ((L + 15) // 16) * 4 + 4)
-    sb = T * (576 * 2 + 368 + 8)
+    # 2 x 241 MB of records alternate: more than the Infinity Cache
+    rows["nvfp4_mla_decode"] = timed_row(
+        torch, lambda i: kvq.decode(caches[i % 2], q, bt, sl, L, c.softmax_scale, k_scale=c.rope_scale, out=out,
+                                    workspace=ws),
+        "hbm", by, HBM_PEAK_GBPS, "GB/s", per=4, sha=sha, batch=c.batch, context=L, heads=c.num_q_heads,
+        roof_extra={"kernels": "mla_decode_kernel + mla_combine_kernel"})
     del caches, q, out
     torch.cuda.empty_cache()
-    rows = nvfp4_prefill_rows(torch, kvq)
-    rows.update({"nvfp4_mla_decode": {"batch": c.batch, "context": L, "heads": c.num_q_heads,
-                                 "us": round(ms * 1e3, 2), "GB_s": round(by / (ms * 1e-3) / 1e9, 1),
-                                 "pct_of_peak": round(100 * by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
-                                 "bytes": by},
-            "nvfp4_store": {"tokens": T, "us": round(ms_store * 1e3, 2),
-                            "tokens_per_s": round(T / (ms_store * 1e-3), 1),
-                            "GB_s": round(sb / (ms_store * 1e-3) / 1e9, 1),
-                            "pct_of_peak": round(100 * sb / (ms_store * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}})
+    rows.update(nvfp4_prefill_rows(torch, kvq))
     return rows
 
 
@@ -434,6 +517,7 @@ def nvfp4_prefill_rows(torch, kvq):
     from workloads import config_nvfp4_mla_prefill
     log("nvfp4 mla prefill")
     c = config_nvfp4_mla_prefill()
+    sha = mla_sha(c)
     dev = "cuda"
     cache = kvq.Nvfp4Cache(c.num_pages)
     kvq.store(cache, c.kv.to(dev), None, torch.from_numpy(c.slot_mapping).to(dev), c.rope_scale)
@@ -442,19 +526,17 @@ def nvfp4_prefill_rows(torch, kvq):
     bt = torch.from_numpy(c.block_table).to(dev)
     sl = torch.from_numpy(c.seq_lens).to(dev)
     out = torch.empty((q.shape[0], c.num_q_heads, 512), dtype=torch.bfloat16, device=dev)
-    ms = timed_mean(torch, lambda: kvq.prefill(cache, q, cu, int(c.q_lens.max()), bt, sl, c.max_seq_len,
-                                               c.softmax_scale, k_scale=c.rope_scale, out=out), reps=5)
     visits = 0
     for L, lq in zip(c.seq_lens, c.q_lens):
         visits += int(np.arange(L - lq + 1, L + 1, dtype=np.int64).sum())
     fl = 2 * (576 + 512) * c.num_q_heads * visits
-    tf = fl / (ms * 1e-3) / 1e12
+    row = timed_row(torch, lambda i: kvq.prefill(cache, q, cu, int(c.q_lens.max()), bt, sl, c.max_seq_len,
+                                                 c.softmax_scale, k_scale=c.rope_scale, out=out),
+                    "mfma", fl, FP16_PEAK_TFLOPS, "TFLOP/s", per=1, sha=sha, batch=c.batch,
+                    new_tokens=int(c.q_lens[0]), context=c.max_seq_len, roof_extra={"dtype": "fp16"})
     del cache
     torch.cuda.empty_cache()
-    return {"nvfp4_mla_prefill": {"batch": c.batch, "new_tokens": int(c.q_lens[0]),
-                                  "context": c.max_seq_len, "us": round(ms * 1e3, 1),
-                                  "TFLOP_s": round(tf, 1), "flops": fl,
-                                  "pct_of_fp16_peak": round(100 * tf / FP16_PEAK_TFLOPS, 2)}}
+    return {"nvfp4_mla_prefill": row}
 
 
 def prefill_flops(seq_lens, q_lens, Hq, D, window=0):
@@ -470,10 +552,28 @@ def prefill_flops(seq_lens, q_lens, Hq, D, window=0):
     return 4 * D * Hq * visits
 
 
+ISSUE_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "issue_counters.md")
+
+
+def issue_record():
+    """MfmaUtil / VALUBusy of the prefill kernels from the committed rocprofv3
+    counter summary, or None when the kernel source changed since."""
+    import hashlib
+    try:
+        line = [l for l in open(ISSUE_PROFILE) if l.startswith("issue_record: ")][0]
+        rec = json.loads(line[len("issue_record: "):])
+        h = hashlib.sha256(open(os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                             rec["kernel_source"]), "rb").read()).hexdigest()
+        return rec["kernels"] if h == rec["kernel_source_sha256"] else None
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+
+
 def prefill_rows(torch, kvq):
-    from workloads import config_chunked_prefill
+    from workloads import config_chunked_prefill, rel_bias_table
     log("chunked prefill")
     c = config_chunked_prefill()
+    sha = case_sha(c)
     dev = "cuda"
     k, v, q = c.k.to(dev), c.v.to(dev), c.q.to(dev)
     slot = torch.from_numpy(c.slot_mapping).to(dev)
@@ -482,50 +582,56 @@ def prefill_rows(torch, kvq):
     cached, new = [torch.from_numpy(i).to(dev) for i in c.store_batches]
     kvq.store(cache, k[cached].contiguous(), v[cached].contiguous(), slot[cached], sc["k"], sc["v"])
     kn, vn, sn = k[new].contiguous(), v[new].contiguous(), slot[new].contiguous()
-    ms_store = timed_mean(torch, lambda: kvq.store(cache, kn, vn, sn, sc["k"], sc["v"]), reps=10)
+    T = int(kn.shape[0])
+    rows = {}
+    rows["store_prefill_new"] = timed_row(torch, lambda i: kvq.store(cache, kn, vn, sn, sc["k"], sc["v"]), "hbm",
+                                          store_bytes(T, c.num_kv_heads, c.head_dim), HBM_PEAK_GBPS, "GB/s",
+                                          per=10, sha=sha, tokens=T)
     del k, v
     bt = torch.from_numpy(c.block_table).to(dev)
     sl = torch.from_numpy(c.seq_lens).to(dev)
     cu = torch.from_numpy(c.cu_q_lens).to(dev)
     slopes = torch.from_numpy(c.slopes).to(dev)
     out = torch.empty_like(q)
-    ms = timed_mean(torch, lambda: kvq.prefill(cache, q, cu, c.max_q_len, bt, sl, c.max_seq_len,
-                                               c.softmax_scale, sc["q"], sc["k"], sc["v"],
-                                               slopes=slopes, out=out), reps=5)
     fl = prefill_flops(c.seq_lens, c.q_lens, c.num_q_heads, c.head_dim)
-    tf = fl / (ms * 1e-3) / 1e12
+    mix = {"dtype": "fp8 QK^T + bf16 PV", "peak_note": "half the flops at each MFMA rate"}
+    issue = issue_record() or {}
+
+    def run(**kw):
+        return lambda i: kvq.prefill(cache, q, cu, c.max_q_len, bt, sl, c.max_seq_len, c.softmax_scale, sc["q"],
+                                     sc["k"], sc["v"], out=out, **kw)
+    shape = {"batch": c.batch, "new_tokens": int(c.q_lens[0]), "context": c.max_seq_len}
+    # without a bias no probability underflows: every block is computed (the
+    # kernel's dense rate)
+    r = timed_row(torch, run(), "mfma", fl, PREFILL_MIXED_PEAK_TFLOPS, "TFLOP/s", per=1, sha=sha,
+                  roof_extra=mix, **shape)
+    r["pct_of_fp8_peak"] = round(100 * r["roofline"]["achieved"] / FP8_PEAK_TFLOPS, 2)
+    if "prefill_e4m3_kernel<0, 0>" in issue:
+        r.update(issue["prefill_e4m3_kernel<0, 0>"])
+    rows["chunked_prefill_nobias"] = r
+    # the slope bias (the workload's main row): blocks whose every probability
+    # is exactly zero are skipped, so the flops are nominal
+    r = timed_row(torch, run(slopes=slopes), "mfma", fl, PREFILL_MIXED_PEAK_TFLOPS, "TFLOP/s", per=1, sha=sha,
+                  roof_extra=dict(mix, flops_kind="nominal: every causal pair, also skipped exact zeros"),
+                  **shape)
+    r["nominal_pct_of_fp8_peak"] = round(100 * r["roofline"]["achieved"] / FP8_PEAK_TFLOPS, 2)
+    if "prefill_e4m3_kernel<1, 0>" in issue:
+        r.update(issue["prefill_e4m3_kernel<1, 0>"])
+    rows["chunked_prefill"] = r
     # the same prefill with a learned relative-bias table of 1,024 entries
-    from workloads import rel_bias_table
     rel = torch.from_numpy(rel_bias_table(np.random.default_rng(6), c.num_q_heads, 1024)).to(torch.bfloat16).to(dev)
-    ms_rel = timed_mean(torch, lambda: kvq.prefill(cache, q, cu, c.max_q_len, bt, sl, c.max_seq_len,
-                                                   c.softmax_scale, sc["q"], sc["k"], sc["v"],
-                                                   out=out, rel_bias=rel), reps=5)
-    # the opt-in single-term e4m3 P variant (slope bias as the main row)
-    ms_p8 = timed_mean(torch, lambda: kvq.prefill(cache, q, cu, c.max_q_len, bt, sl, c.max_seq_len,
-                                                  c.softmax_scale, sc["q"], sc["k"], sc["v"],
-                                                  slopes=slopes, out=out, fp8_p=True), reps=5)
-    # the same prefill without a bias: no probability underflows, every block
-    # is computed (the dense rate of the kernel)
-    ms_nb = timed_mean(torch, lambda: kvq.prefill(cache, q, cu, c.max_q_len, bt, sl, c.max_seq_len,
-                                                  c.softmax_scale, sc["q"], sc["k"], sc["v"], out=out), reps=5)
-    T = int(kn.shape[0])
+    r = timed_row(torch, run(rel_bias=rel), "mfma", fl, PREFILL_MIXED_PEAK_TFLOPS, "TFLOP/s", per=1, sha=sha,
+                  roof_extra=mix, **shape)
+    rows["chunked_prefill_rel1024"] = r
+    # P variants on fp8 MFMA (slope bias): one e4m3 term (opt-in, looser
+    # tolerance) and two e4m3 terms (the measured alternative to bf16 P)
+    for name, kw in (("chunked_prefill_fp8p", {"fp8_p": True}), ("chunked_prefill_fp8p2", {"fp8_p2": True})):
+        r = timed_row(torch, run(slopes=slopes, **kw), "mfma", fl, FP8_PEAK_TFLOPS, "TFLOP/s", per=1, sha=sha,
+                      roof_extra={"dtype": "fp8", "flops_kind": "nominal"}, **shape)
+        rows[name] = r
     del cache
     torch.cuda.empty_cache()
-    return {"chunked_prefill_nobias": {"us": round(ms_nb * 1e3, 1),
-                                       "TFLOP_s": round(fl / (ms_nb * 1e-3) / 1e12, 1),
-                                       "pct_of_fp8_peak": round(100 * fl / (ms_nb * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 2)},
-            "chunked_prefill": {"batch": c.batch, "new_tokens": int(c.q_lens[0]),
-                                "context": c.max_seq_len, "us": round(ms * 1e3, 1),
-                                "TFLOP_s": round(tf, 1), "flops": fl,
-                                "pct_of_fp8_peak": round(100 * tf / FP8_PEAK_TFLOPS, 2)},
-            "chunked_prefill_fp8p": {"us": round(ms_p8 * 1e3, 1),
-                                     "TFLOP_s": round(fl / (ms_p8 * 1e-3) / 1e12, 1),
-                                     "pct_of_fp8_peak": round(100 * fl / (ms_p8 * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 2)},
-            "chunked_prefill_rel1024": {"us": round(ms_rel * 1e3, 1),
-                                        "TFLOP_s": round(fl / (ms_rel * 1e-3) / 1e12, 1),
-                                        "pct_of_fp8_peak": round(100 * fl / (ms_rel * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 2)},
-            "store_prefill_new": {"tokens": T, "us": round(ms_store * 1e3, 2),
-                                  "tokens_per_s": round(T / (ms_store * 1e-3), 1)}}
+    return rows
 
 
 def long_context_rows(torch, kvq):
@@ -533,6 +639,7 @@ def long_context_rows(torch, kvq):
     out = {}
     log("long-context decode")
     c = config_long_context()
+    sha = case_sha(c)
     dev = "cuda"
     k, v, q = c.k.to(dev), c.v.to(dev), c.q.to(dev)
     slot = torch.from_numpy(c.slot_mapping).to(dev)
@@ -544,23 +651,87 @@ def long_context_rows(torch, kvq):
         kvq.store(cache, k, v, slot, sc["k"], sc["v"])
     del k, v
     B, Hq, Hkv, D, L = c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim, c.max_seq_len
+    outb = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
     for w in (0, 512):
-        it = [0]
-
-        def run():
-            cache = caches[it[0] % 2]
-            it[0] += 1
-            kvq.decode(cache, q, bt, sl, L, c.softmax_scale, sc["q"], sc["k"], sc["v"], window=w)
-        ms = timed_mean(torch, run, reps=10)
+        ws = torch.zeros(max(kvq.decode_workspace_bytes(caches[0], B, L, Hq, window=w), 1), dtype=torch.uint8,
+                         device=dev)
         att = min(L, w) if w else L
         by = decode_bytes(B, Hq, Hkv, D, att)
-        out["long_context" + ("_window512" if w else "")] = {
-            "batch": B, "context": L, "attended": att, "us": round(ms * 1e3, 2),
-            "GB_s": round(by / (ms * 1e-3) / 1e9, 1),
-            "pct_of_peak": round(100 * by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+        out["long_context" + ("_window512" if w else "")] = timed_row(
+            torch, lambda i, w=w, ws=ws: kvq.decode(caches[i % 2], q, bt, sl, L, c.softmax_scale, sc["q"], sc["k"],
+                                                    sc["v"], window=w, out=outb, workspace=ws),
+            "hbm", by, HBM_PEAK_GBPS, "GB/s", per=5, sha=sha, batch=B, context=L, attended=att,
+            **({"note": "latency-bound"} if w else {}))
     del caches
     torch.cuda.empty_cache()
     return out
+
+
+def mla_decode_only(torch, kvq):
+    """The NVFP4 store and MLA decode rows without the prefill row (profiling)."""
+    saved = globals()["nvfp4_prefill_rows"]
+    globals()["nvfp4_prefill_rows"] = lambda torch, kvq: {}
+    try:
+        return nvfp4_rows(torch, kvq)
+    finally:
+        globals()["nvfp4_prefill_rows"] = saved
+
+
+def tier1_rows(torch, kvq):
+    """The two attention shapes of the vLLM PR 54705 evidence document ("Tier
+    1: kernel performance") not covered by the workloads above:
+    decode_kv65536_b1_tp4 (one sequence over 65,536 keys, 16/2 heads) and
+    local_prefill_q8192_tp1 (8,192 new tokens, window 512, 64/8 heads, learned
+    bias of extent 128)."""
+    from workloads import config_single_stream_decode, config_local_prefill
+    log("tier-1 shapes")
+    dev = "cuda"
+    rows = {}
+    c = config_single_stream_decode()
+    sha = case_sha(c)
+    k, v, q = c.k.to(dev), c.v.to(dev), c.q.to(dev)
+    slot = torch.from_numpy(c.slot_mapping).to(dev)
+    sc = {n: float(kvq.calibrate_amax(x)[1].item()) for n, x in (("k", k), ("v", v), ("q", q))}
+    # 10 copies of the 33.5 MB cache rotate, 335 MB: more than the Infinity Cache
+    caches = [kvq.E4M3Cache(c.num_pages, c.num_kv_heads, c.head_dim) for _ in range(10)]
+    for cache in caches:
+        kvq.store(cache, k, v, slot, sc["k"], sc["v"])
+    del k, v
+    bt = torch.from_numpy(c.block_table).to(dev)
+    sl = torch.from_numpy(c.seq_lens).to(dev)
+    L, Hq, Hkv, D = c.max_seq_len, c.num_q_heads, c.num_kv_heads, c.head_dim
+    outb = torch.empty((1, Hq, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(max(kvq.decode_workspace_bytes(caches[0], 1, L, Hq), 1), dtype=torch.uint8, device=dev)
+    rows["single_stream_decode"] = timed_row(
+        torch, lambda i: kvq.decode(caches[i % 10], q, bt, sl, L, c.softmax_scale, sc["q"], sc["k"], sc["v"],
+                                    out=outb, workspace=ws),
+        "hbm", decode_bytes(1, Hq, Hkv, D, L), HBM_PEAK_GBPS, "GB/s", per=10, sha=sha, batch=1, context=L,
+        q_heads=Hq, kv_heads=Hkv)
+    del caches
+    torch.cuda.empty_cache()
+    c = config_local_prefill()
+    sha = case_sha(c)
+    k, v, q = c.k.to(dev), c.v.to(dev), c.q.to(dev)
+    slot = torch.from_numpy(c.slot_mapping).to(dev)
+    sc = {n: float(kvq.calibrate_amax(x)[1].item()) for n, x in (("k", k), ("v", v), ("q", q))}
+    cache = kvq.E4M3Cache(c.num_pages, c.num_kv_heads, c.head_dim)
+    kvq.store(cache, k, v, slot, sc["k"], sc["v"])
+    del k, v
+    bt = torch.from_numpy(c.block_table).to(dev)
+    sl = torch.from_numpy(c.seq_lens).to(dev)
+    cu = torch.from_numpy(c.cu_q_lens).to(dev)
+    rel = torch.from_numpy(c.rel).to(torch.bfloat16).to(dev)
+    out = torch.empty_like(q)
+    fl = prefill_flops(c.seq_lens, c.q_lens, c.num_q_heads, c.head_dim, window=c.window)
+    rows["local_prefill"] = timed_row(
+        torch, lambda i: kvq.prefill(cache, q, cu, c.max_q_len, bt, sl, c.max_seq_len, c.softmax_scale, sc["q"],
+                                     sc["k"], sc["v"], window=c.window, rel_bias=rel, out=out),
+        "mfma", fl, PREFILL_MIXED_PEAK_TFLOPS, "TFLOP/s", per=2, sha=sha,
+        roof_extra={"dtype": "fp8 QK^T + bf16 PV"}, new_tokens=int(c.q_lens[0]), window=c.window,
+        q_heads=c.num_q_heads, kv_heads=c.num_kv_heads, rel_extent=int(c.rel.shape[1]))
+    del cache
+    torch.cuda.empty_cache()
+    return rows
 
 
 def cpu_baseline(c):

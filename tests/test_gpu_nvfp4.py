@@ -120,9 +120,10 @@ def test_mla_decode_zero_length_and_poison():
     check_attention(out, ref, "mla zero/poison")
 
 
-@pytest.mark.parametrize("layer", [0, 1])
+@pytest.mark.parametrize("layer", [0, 1, 2, 3])
 def test_mla_decode_full_size_sampled(layer):
-    """Batch 32 x 16,384 tokens; four sequences compared with the oracle."""
+    """Batch 32 x 16,384 tokens, each of the four layer stds (0.05, 4 and two
+    uniform draws); four sequences compared with the oracle."""
     c = config_nvfp4_mla(layer=layer)
     out, ref = run_mla(c, seqs=[0, 7, 19, 31])
     print(check_attention(out, ref, "nvfp4 mla layer %d" % layer))

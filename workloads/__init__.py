@@ -26,6 +26,9 @@ from .gen import (  # noqa: F401
     config_batched_decode,
     config_long_context,
     config_chunked_prefill,
+    config_single_stream_decode,
+    config_local_prefill,
+    write_path_tokens,
     config_nvfp4_mla,
     config_nvfp4_mla_prefill,
     geometric_slopes,

@@ -244,6 +244,41 @@ def config_chunked_prefill(seed: int = 3, cached: int = 32768, new: int = 2048,
                           slopes=geometric_slopes(32))
 
 
+# --------------------------------------------------------------------------
+# Shapes of the vLLM PR 54705 evidence document, "Tier 1: kernel
+# performance": the model there has 8 KV heads of head_dim 128 (so 2 per rank
+# at TP4 and 8 at TP1), sliding-window layers of 512 tokens and a learned
+# relative bias (extent 128 in the sliding-window tests). Query heads are not
+# given; these take a GQA group of 8, as the other workloads.
+# --------------------------------------------------------------------------
+
+def config_single_stream_decode(seed: int = 7) -> AttnCase:
+    """One sequence decoding over 65,536 cached tokens with a rank's TP4 share
+    (decode_kv65536_b1_tp4): 16 query / 2 KV heads, head_dim 128, the batched
+    decode generators, calibrated scales."""
+    return make_attn_case("single_stream_decode", seed, [65536], [1], 16, 2, 128, qk_dist="rms20",
+                          v_std=8.0, v_outlier_frac=1e-3, split_store_at_new=False)
+
+
+def config_local_prefill(seed: int = 8) -> AttnCase:
+    """A sliding-window (local) prefill of 8,192 new tokens on TP1 shapes
+    (local_prefill_q8192_tp1): 64 query / 8 KV heads, head_dim 128, window
+    512, a learned relative-bias table of extent 128, N(0,1) Q/K/V,
+    calibrated scales. The sequence has no earlier tokens."""
+    return make_attn_case("local_prefill", seed, [8192], [8192], 64, 8, 128, window=512,
+                          rel_extent=128)
+
+
+def write_path_tokens(seed: int, n: int, num_kv_heads: int, head_dim: int = 128):
+    """K/V tokens of the write-path sweep ("Tier 1": 33, 2,048 and 16,384
+    tokens per call, two head configurations): n tokens of the batched-decode
+    value distributions, written to pages of a fresh pool in random order.
+    Returns (k, v, slot_mapping, num_pages)."""
+    c = make_attn_case("write_path", seed, [n], [1], num_kv_heads, num_kv_heads, head_dim,
+                       qk_dist="rms20", v_std=8.0, v_outlier_frac=1e-3, split_store_at_new=False)
+    return c.k, c.v, c.slot_mapping, c.num_pages
+
+
 @dataclass
 class MlaCase:
     """NVFP4 MLA latent-cache decode workload."""
@@ -325,6 +360,8 @@ def config_nvfp4_mla_prefill(seed: int = 5, batch: int = 4, context: int = 16384
 
 
 CONFIGS = {
+    "single_stream_decode": config_single_stream_decode,
+    "local_prefill": config_local_prefill,
     "tiny_decode": config_tiny_decode,
     "batched_decode": config_batched_decode,
     "long_context": config_long_context,
