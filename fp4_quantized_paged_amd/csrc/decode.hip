@@ -25,6 +25,9 @@
 //    bytes per dim per page), B = P. P = 256 * p is split into two e4m3 terms
 //    (hi = e4m3(P), lo = e4m3(P - hi)) accumulated by two MFMAs, which keeps
 //    the relative error of each weight near 2^-8 while staying on fp8 MFMA;
+//    a ones tile in the same MFMA stream sums the two terms into the
+//    normaliser, so a weight too small for both terms is dropped from the
+//    numerator and the denominator alike;
 //  * V^T operands come straight from HBM with 16-byte loads (the cache
 //    layout makes each operand slice contiguous). With head_dim 128 the K
 //    rows of a block are fetched as whole 128-byte lines into a per-wave LDS
@@ -133,7 +136,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   const float qpos = (float)(L - 1);
 
   float m_run = -INFINITY;   // running max, log2 domain
-  float l_run = 0.0f;        // this lane's partial sum of 2^8 p
+  // row sums of P as PV sums them (a ones tile on fp8 MFMA over both e4m3
+  // terms): every element of lane (row, grp) holds the sum for query `row`
+  v4f ol = v4f{0.f, 0.f, 0.f, 0.f};
+  const v8i ones8 = v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                        0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
   v4f o[kTiles];
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -324,22 +331,17 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     // P = 2^8 p (exponent offset 8), split into two e4m3 terms
     const float off = 8.0f - m_use;
     v8i phi, plo;
-    float psum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[j][i], scale, off));
-        psum += p[i];
-      }
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[j][i], scale, off));
       const uint32_t hi = cvt4_e4m3(p[0], p[1], p[2], p[3]);
       const v2f h01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
       const v2f h23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
       phi[j] = (int)hi;
       plo[j] = (int)cvt4_e4m3(p[0] - h01.x, p[1] - h01.y, p[2] - h23.x, p[3] - h23.y);
     }
-    l_run = l_run * alpha + psum;
 
     // ---- zero V bytes of tokens outside [lo, L) (stale, NaN or clamped pages:
     // 0 * NaN would poison the MFMA)
@@ -361,17 +363,18 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     if (__ballot(alpha != 1.0f)) {
 #pragma unroll
       for (int t = 0; t < kTiles; ++t) o[t] *= alpha;
+      ol *= alpha;
     }
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       o[t] = mfma_16x16x128_e4m3(vop[t], phi, o[t]);
       o[t] = mfma_16x16x128_e4m3(vop[t], plo, o[t]);
     }
+    // the normaliser sums the same rounded terms as PV
+    ol = mfma_16x16x128_e4m3(ones8, phi, ol);
+    ol = mfma_16x16x128_e4m3(ones8, plo, ol);
   }
-
-  // ---- per-row sum of p across the four key groups
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  const float l_run = ol[0];
 
   // ---- merge the W waves through LDS, in wave order (deterministic). Each
   // wave parks m, l and its unnormalised O (lane: query row, dims

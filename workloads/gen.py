@@ -157,7 +157,8 @@ def make_attn_case(name: str, seed: int, seq_lens, q_lens, num_q_heads: int,
                    slopes: Optional[np.ndarray] = None, fixed_scales: Optional[dict] = None,
                    v_scale_override: Optional[float] = None, spare_frac: float = 0.25,
                    min_pool: int = 0, split_store_at_new: bool = True,
-                   softmax_scale: Optional[float] = None, rel_extent: int = 0) -> AttnCase:
+                   softmax_scale: Optional[float] = None, rel_extent: int = 0,
+                   v_mean: float = 0.0) -> AttnCase:
     """Draw Q, K, V and a random page layout.
 
     qk_dist: "normal" for N(0,1), "rms20" for per-row RMS-normed N(0,1) scaled
@@ -180,6 +181,8 @@ def make_attn_case(name: str, seed: int, seq_lens, q_lens, num_q_heads: int,
     else:
         raise ValueError(qk_dist)
     v = _normal(rng, (T, num_kv_heads, head_dim), v_std)
+    if v_mean:
+        v = v + np.float32(v_mean)
     n_out = _add_outliers(rng, v, v_outlier_frac, *v_outlier_range) if v_outlier_frac > 0 else 0
     bt, num_pages, slot, seq_of, pos_of = paged_layout(rng, seq_lens, PAGE_SIZE, spare_frac, min_pool)
     # store order: tokens already cached first, then the new (query) tokens
