@@ -21,12 +21,15 @@
 //    of two that puts its largest element in [2^13, 2^14); exact for all but
 //    elements 2^-31 below the head maximum);
 //  * the dequantized rows also go to LDS (16 KB per wave, chunk-major and
-//    bank-conflict free); after one workgroup barrier each wave of a pair
-//    takes half of the 512 latent dims of PV over both of the pair's pages:
-//    v_mfma_f32_16x16x32_f16 with A = V^T (two ds_read_b64_tr_b16 16-lane
-//    transposes, four keys of each page) and B = the two pages' P, which the
-//    pair exchanges through LDS in fp16. A second barrier per step keeps the
-//    rows until both halves have read them;
+//    bank-conflict free); once the partner's counter shows its rows and P of
+//    the step in place, each wave of a pair takes half of the 512 latent dims
+//    of PV over both of the pair's pages: v_mfma_f32_16x16x32_f16 with
+//    A = V^T (two ds_read_b64_tr_b16 16-lane transposes, four keys of each
+//    page) and B = the two pages' P, which the pair exchanges through LDS in
+//    fp16. The partner's next counter value tells a wave that its rows have
+//    been read before it overwrites them (no workgroup barrier in the page
+//    loop; the waits are bounded, and a wave that gives up turns the
+//    workgroup's outputs into NaN instead of hanging);
 //  * P enters PV in fp16 as 2^(x - m) * s2 * 2^-Gs. Per pair and head, the
 //    running max m is integer-valued and raised only when a score passes it
 //    by more than 8 (log2 units); Gs is the largest exponent of the outer
