@@ -218,12 +218,6 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     r.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off_s2, 0, 0));
   };
   PageOp bufs[kBufs];
-#pragma unroll
-  for (int k = 0; k < kBufs; ++k) {
-    const int p = p_begin + kStepPages * k + wpos;
-    fetch_page(p < p_end, __builtin_amdgcn_readlane(btw, kStepPages * k + wpos), bufs[k]);
-  }
-  __builtin_amdgcn_sched_barrier(0);
 
   // ---- Q: stage bf16 in LDS, find each head's power-of-two scale k (largest
   // element of head h times 2^k in [2^13, 2^14)), and form this lane's
@@ -246,6 +240,14 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
       qs[h * kStageRowU4 + (c - h * ((kLat + 64) / 8))] = qv[j];
     }
     __syncthreads();
+    // the first pages' record bytes, requested once Q is staged (the loads
+    // of Q are then not waited for together with them)
+#pragma unroll
+    for (int k = 0; k < kBufs; ++k) {
+      const int p = p_begin + kStepPages * k + wpos;
+      fetch_page(p < p_end, __builtin_amdgcn_readlane(btw, kStepPages * k + wpos), bufs[k]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (wave == 0) {
       const uint4 *qr = qs + row * kStageRowU4;
       uint32_t am = 0;
@@ -338,6 +340,10 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
 
   // Step k: page p = p_begin + 8k + wpos of this wave.
   auto step = [&](PageOp &op, int k) {
+    // the two waves of a SIMD take turns at the higher issue priority, step
+    // by step (the older wave would otherwise always win the arbitration)
+    if (((k + (wave >> 2)) & 1) != 0) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     const int p = p_begin + kStepPages * k + wpos;
     // a page past the split, or the sequence's last, partial page: some or
     // all keys masked (uniform over the wave)
