@@ -444,6 +444,9 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     pair_wait(2 * k + 1);   // the partner's rows and P of the step are in place
     __builtin_amdgcn_sched_barrier(0);
     // ---- PV over the pair's two pages, this wave's half of the latent
+    // (the highest priority while the multiplies issue, so the other wave of
+    // the SIMD fills the matrix unit's busy cycles with its vector work)
+    __builtin_amdgcn_s_setprio(2);
     v4h pother = __builtin_bit_cast(v4h, s_p[partner][lane]);
     const float m_other = s_mp[partner][row];
     const int g_other = s_gp[partner];
@@ -491,6 +494,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
       // hoist all of them (64 registers)
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     pair_publish(2 * k + 2);
   };
 
