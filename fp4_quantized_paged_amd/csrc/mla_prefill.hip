@@ -460,7 +460,11 @@ __global__ __launch_bounds__(kThreads) void mla_prefill_kernel(DecodeMlaLaunch a
     // the record bytes of step k+2 are requested before PV of step k and
     // dequantized after it (not held in registers through QK^T and softmax)
     if (k + 2 < nsteps) fetch(k + 2, ra);
+    // PV at the highest wave priority: the other wave of the SIMD fills the
+    // matrix unit's busy cycles with its vector work
+    __builtin_amdgcn_s_setprio(2);
     pv_step(k);
+    __builtin_amdgcn_s_setprio(0);
     if (k + 2 < nsteps) dequant(k + 2, ra);
     if (k + 1 < nsteps) {
       qk_softmax(k + 1);
