@@ -90,13 +90,25 @@ kvq::DecodePlan plan_decode(const kvq_cache *c, int32_t num_seqs, int32_t max_se
   // the smallest power of two of waves that gives each wave at most one block
   // of a short sequence (so one split suffices and no combine runs), else 8
   pl.waves = nblk > 4 ? 8 : (nblk > 2 ? 4 : (nblk > 1 ? 2 : 1));
+  auto splits_for = [&](int64_t w) {
+    int64_t sp = (target_waves + units * w - 1) / (units * w);
+    const int64_t max_by_waves = (nblk + w - 1) / w;  // >= 1 block per wave
+    return sp < max_by_waves ? sp : max_by_waves;
+  };
   int64_t splits;
   if (p->num_splits > 0) {
     splits = p->num_splits;
   } else {
-    splits = (target_waves + units * pl.waves - 1) / (units * pl.waves);
-    const int64_t max_by_waves = (nblk + pl.waves - 1) / pl.waves;  // >= 1 block per wave
-    if (splits > max_by_waves) splits = max_by_waves;
+    splits = splits_for(pl.waves);
+    // few (sequence, KV head) units over long sequences: fewer waves per
+    // workgroup and more splits, so that the workgroups still cover every
+    // compute unit (short sequences keep their single split: no combine)
+    while (nblk > 8 && pl.waves > 1 && units * splits < current_cu_count()) {
+      const int64_t s2 = splits_for(pl.waves / 2);
+      if (s2 <= splits) break;
+      pl.waves /= 2;
+      splits = s2;
+    }
   }
   if (splits > nblk) splits = nblk;
   if (splits < 1) splits = 1;

@@ -10,52 +10,85 @@
 
 namespace kvq {
 
+// One workgroup per (sequence, query head): kCombineGroups thread groups of D
+// threads (one per dim) take consecutive ranges of the splits, so a long
+// split list is read by four times the threads; each thread requests kPre
+// splits' partials before it uses any (one memory round trip per kPre
+// splits). Order of operations, fixed for every launch: M is the max of all
+// m_s; each group sums its range in split order; the four group sums are
+// added in group order.
+constexpr int kCombineGroups = 4;
+
 template <int D>
-__global__ __launch_bounds__(D) void split_combine_kernel(const float *part_o, const float *part_ml,
-                                                          uint16_t *out, int splits, float v_scale) {
-  // Up to kPre splits: every partial is requested before any is used (one
-  // memory round trip); more splits take the plain loops. Both orders of
-  // operations are the same: the max first, then the sums in split order.
+__global__ __launch_bounds__(D * kCombineGroups) void split_combine_kernel(const float *part_o, const float *part_ml,
+                                                                           uint16_t *out, int splits, float v_scale) {
   constexpr int kPre = 16;
+  __shared__ float s_m[kCombineGroups];
+  __shared__ float s_acc[kCombineGroups][D];
+  __shared__ float s_den[kCombineGroups][D];
   const int bh = blockIdx.x;          // b * hq + h
-  const int dcol = threadIdx.x;
+  const int dcol = threadIdx.x % D;
+  const int g = threadIdx.x / D;
+  const int per = (splits + kCombineGroups - 1) / kCombineGroups;
+  const int s0 = min(g * per, splits);
+  const int s1 = min(s0 + per, splits);
   const float *ml = part_ml + (size_t)bh * splits * 2;
   const float *po = part_o + (size_t)bh * splits * D + dcol;
+
+  // the group's max; its first kPre splits' partials are requested with it
+  float mv[kPre], lv[kPre], ov[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int c = min(s0 + i, splits - 1);   // clamped copies past the range are not used
+    mv[i] = ml[2 * c];
+    lv[i] = ml[2 * c + 1];
+    ov[i] = po[(size_t)c * D];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kPre; ++i)
+    if (s0 + i < s1) M = fmaxf(M, mv[i]);
+  for (int s = s0 + kPre; s < s1; ++s) M = fmaxf(M, ml[2 * s]);
+  if (dcol == 0) s_m[g] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  const float Mu = M == -INFINITY ? 0.0f : M;
+
   float acc = 0.0f, den = 0.0f;
-  if (splits <= kPre) {
-    float mv[kPre], lv[kPre], ov[kPre];
 #pragma unroll
-    for (int s = 0; s < kPre; ++s) {
-      const int c = min(s, splits - 1);   // clamped copies past the last split are not used
-      mv[s] = ml[2 * c];
-      lv[s] = ml[2 * c + 1];
-      ov[s] = po[(size_t)c * D];
-    }
-    float M = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < kPre; ++s)
-      if (s < splits) M = fmaxf(M, mv[s]);
-    const float Mu = M == -INFINITY ? 0.0f : M;
-#pragma unroll
-    for (int s = 0; s < kPre; ++s) {
-      if (s < splits) {
-        const float f = __builtin_amdgcn_exp2f(mv[s] - Mu);
-        acc += f * ov[s];
-        den += f * lv[s];
-      }
-    }
-  } else {
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[2 * s]);
-    const float Mu = M == -INFINITY ? 0.0f : M;
-    for (int s = 0; s < splits; ++s) {
-      const float f = __builtin_amdgcn_exp2f(ml[2 * s] - Mu);
-      acc += f * po[(size_t)s * D];
-      den += f * ml[2 * s + 1];
+  for (int i = 0; i < kPre; ++i) {
+    if (s0 + i < s1) {
+      const float f = __builtin_amdgcn_exp2f(mv[i] - Mu);
+      acc += f * ov[i];
+      den += f * lv[i];
     }
   }
-  const float val = den > 0.0f ? (acc / den) * v_scale : 0.0f;
-  out[(size_t)bh * D + dcol] = (uint16_t)f32_to_bf16_bits(val);
+  for (int sb = s0 + kPre; sb < s1; sb += kPre) {
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      const int c = min(sb + i, splits - 1);
+      mv[i] = ml[2 * c];
+      lv[i] = ml[2 * c + 1];
+      ov[i] = po[(size_t)c * D];
+    }
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      if (sb + i < s1) {
+        const float f = __builtin_amdgcn_exp2f(mv[i] - Mu);
+        acc += f * ov[i];
+        den += f * lv[i];
+      }
+    }
+  }
+  s_acc[g][dcol] = acc;
+  s_den[g][dcol] = den;
+  __syncthreads();
+  if (g == 0) {
+    acc = ((s_acc[0][dcol] + s_acc[1][dcol]) + s_acc[2][dcol]) + s_acc[3][dcol];
+    den = ((s_den[0][dcol] + s_den[1][dcol]) + s_den[2][dcol]) + s_den[3][dcol];
+    const float val = den > 0.0f ? (acc / den) * v_scale : 0.0f;
+    out[(size_t)bh * D + dcol] = (uint16_t)f32_to_bf16_bits(val);
+  }
 }
 
 }  // namespace kvq
