@@ -443,7 +443,7 @@ hipError_t launch_decode_t(const DecodeE4M3Launch &a, const DecodePlan &p, hipSt
                      p.splits, p.blocks_per_split, p.qtiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL((split_combine_kernel<D>), dim3((unsigned)((size_t)a.batch * a.hq)), dim3(D * kCombineGroups), 0, s,
+  hipLaunchKernelGGL((split_combine_kernel<D>), dim3((unsigned)((size_t)a.batch * a.hq)), dim3(D * combine_groups(p.splits)), 0, s,
                      a.part_o, a.part_ml, a.out, p.splits, a.v_scale);
   return hipGetLastError();
 }
