@@ -69,7 +69,7 @@ constexpr int kStepPages = kWaves;                // pages per workgroup step
 // Spins of a pair wait before the wave gives up (each spin sleeps ~64
 // cycles; a normal wait takes a few spins).
 constexpr int kSpinLimit = 1 << 22;
-constexpr int kQReg = 4;                          // latent QK^T steps whose Q operand stays in registers
+constexpr int kQReg = 16;                         // latent QK^T steps whose Q operand stays in registers
 constexpr int kQLds = 16 + 2 - kQReg;             // the other latent steps and the 2 RoPE steps: from LDS
 
 // LDS: the latent rows of each wave's page. Before the loop the region holds
@@ -157,6 +157,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
   __shared__ int s_gp[kWaves];                        // the Gs that P was taken against
   __shared__ float s_m[kPairs][kHeads], s_e[kPairs][kHeads], s_l[kWaves][kHeads];
   __shared__ int s_k[kHeads];
+  __shared__ v4f s_hf[kHeads];                        // per head: output scale, or (M, den, E) of the split
   __shared__ int s_flag[kWaves];                      // pair handshake counters
   __shared__ int s_err;                               // a pair wait gave up
   __shared__ int s_bt[kMaxSplitPages];                // this split's block-table slice
@@ -456,16 +457,23 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
       va0[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(rd0 + 512 * q));
       va1[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(rd1 + 512 * q));
     };
-#pragma unroll
-    for (int q = 0; q < kLook; ++q) read_tile(q);
     // the pair's common m and Gs after this step; rescales are powers of two
     const float m_new = fmaxf(m_self, m_other);
     const int g_new = max(g_self, g_other);
-    if (__ballot(m_new != m_run || g_new != Gs)) {
-      const float e_new = m_new + (float)g_new;
-      const float f_o = (m_run == -INFINITY || Gs == kGUnset) ? 0.0f : pow2i(m_run + (float)Gs - e_new);
+    // the accumulator rescale is a branch of its own, ahead of everything
+    // else the rescale changes: with more work in the same branch the
+    // compiler moved all 64 accumulator registers at the join on every step
+    const bool resc = __ballot(m_new != m_run || g_new != Gs) != 0;
+    if (resc) {
+      const float f_o =
+          (m_run == -INFINITY || Gs == kGUnset) ? 0.0f : pow2i(m_run + (float)Gs - (m_new + (float)g_new));
 #pragma unroll
       for (int t = 0; t < 16; ++t) o[t] *= f_o;
+    }
+#pragma unroll
+    for (int q = 0; q < kLook; ++q) read_tile(q);
+    if (resc) {
+      const float e_new = m_new + (float)g_new;
       l_run = (m_run == -INFINITY ? 0.0f : l_run * pow2i(m_run - m_new)) +
               (m_self == -INFINITY ? 0.0f : psum * pow2i(m_self - m_new));
       const float f_self = (m_self == -INFINITY || g_self == kGUnset) ? 0.0f : pow2i(m_self + (float)g_self - e_new);
@@ -534,6 +542,28 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
 #pragma unroll
     for (int q = 0; q < 16; ++q) o[q] *= f;
   }
+  // the per-head factors of the output pass, once per head: M and E are the
+  // largest of the four pairs' m and m + Gs, den = sum over pairs of
+  // 2^(m - M) (l_half0 + l_half1); with one split the output scale is
+  // 2^(E - M) / den
+  if (wave == 0 && lane < kHeads) {
+    const int hd = lane;
+    float Mh = -INFINITY, Eh = -INFINITY, den = 0.0f;
+#pragma unroll
+    for (int pr = 0; pr < kPairs; ++pr) {
+      Mh = fmaxf(Mh, s_m[pr][hd]);
+      Eh = fmaxf(Eh, s_e[pr][hd]);
+    }
+    if (Mh != -INFINITY) {
+#pragma unroll
+      for (int pr = 0; pr < kPairs; ++pr)
+        if (s_m[pr][hd] != -INFINITY)
+          den += __builtin_amdgcn_exp2f(s_m[pr][hd] - Mh) * (s_l[2 * pr][hd] + s_l[2 * pr + 1][hd]);
+    }
+    float sc = 0.0f;
+    if (den > 0.0f && Eh != -INFINITY) sc = __builtin_ldexpf(1.0f / den, (int)(Eh - Mh));
+    s_hf[hd] = splits == 1 ? v4f{sc, 0.0f, 0.0f, 0.0f} : v4f{Mh, den, Eh, 0.0f};
+  }
   // every wave leaves its scaled half of O in LDS (tile-major, lane-minor:
   // conflict-free 16-byte writes); the output pass adds the four pairs
   v4f *slab = (v4f *)smem;   // [wave][16 tiles][64 lanes]
@@ -552,21 +582,9 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int pr = 0; pr < kPairs; ++pr) acc += slab[((2 * pr + h) * 16 + q) * 64 + ln];
-    float Mh = -INFINITY, Eh = -INFINITY, den = 0.0f;
-#pragma unroll
-    for (int pr = 0; pr < kPairs; ++pr) {
-      Mh = fmaxf(Mh, s_m[pr][hd]);
-      Eh = fmaxf(Eh, s_e[pr][hd]);
-    }
-    if (Mh != -INFINITY) {
-#pragma unroll
-      for (int pr = 0; pr < kPairs; ++pr)
-        if (s_m[pr][hd] != -INFINITY)
-          den += __builtin_amdgcn_exp2f(s_m[pr][hd] - Mh) * (s_l[2 * pr][hd] + s_l[2 * pr + 1][hd]);
-    }
+    const v4f hf = s_hf[hd];
     if (splits == 1) {
-      float sc = 0.0f;
-      if (den > 0.0f && Eh != -INFINITY) sc = __builtin_ldexpf(1.0f / den, (int)(Eh - Mh));
+      const float sc = hf[0];
       uint2 w;
       w.x = f32_to_bf16_bits(acc[0] * sc) | (f32_to_bf16_bits(acc[1] * sc) << 16);
       w.y = f32_to_bf16_bits(acc[2] * sc) | (f32_to_bf16_bits(acc[3] * sc) << 16);
@@ -575,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
     } else {
       const size_t pi = ((size_t)b * a.hq + hd) * splits + split;
       *(v4f *)(a.part_o + pi * kLat + d) = failed ? v4f{NAN, NAN, NAN, NAN} : acc;
-      if (d == 0) *(v4f *)(a.part_ml + 4 * pi) = v4f{Mh, den, Eh, 0.0f};
+      if (d == 0) *(v4f *)(a.part_ml + 4 * pi) = hf;
     }
   }
 }
