@@ -131,7 +131,7 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
   __shared__ PrefillSmem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row = lane & 15;
   const int grp = lane >> 4;
 
@@ -224,18 +224,25 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
 
   // ---- block loader: thread chunk q in [0, 2048): q < 1024 -> K, else V^T;
   // 128 chunks (2 KB) per page. Pages past the sequence end are clamped.
+  // Chunk c of a thread lies in block page (wave / 2) + 4 (c & 1), so a wave
+  // needs two page ids per block; they are read a block ahead (fetch_ids),
+  // which keeps the block-table round trip out of the loads' issue.
+  static_assert(kLoadChunks == 4 && 64 * kPW == 512, "chunk -> page mapping");
   uint4 pre[kLoadChunks];
-  auto load_block = [&](int blk) {
+  int ids[2];
+  auto fetch_ids = [&](int blk) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) ids[h] = bt[min(blk * 8 + (wave >> 1) + 4 * h, page_last)];
+  };
+  auto load_block = [&]() {
 #pragma unroll
     for (int c = 0; c < kLoadChunks; ++c) {
       const int q = tid + c * 64 * kPW;
       const int tensor = q >> 10;
-      const int pg = (q >> 7) & 7;
       const int off = (q & 127) << 4;
-      const int page = min(blk * 8 + pg, page_last);
       const uint8_t *base = tensor == 0 ? a.kc : a.vc;
-      const v4u x = __builtin_nontemporal_load(
-          (const v4u *)(base + (size_t)bt[page] * page_stride + (size_t)g * head_stride + off));
+      const size_t page_off = (size_t)__builtin_amdgcn_readfirstlane(ids[c & 1]) * page_stride;
+      const v4u x = __builtin_nontemporal_load((const v4u *)(base + page_off + (size_t)g * head_stride + off));
       pre[c] = make_uint4(x.x, x.y, x.z, x.w);
     }
   };
@@ -287,10 +294,14 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
   };
 
   const float fold = a.fold_log2;
-  if (blk_lo <= blk_hi) load_block(blk_hi);   // empty when seq_lens < new tokens
+  if (blk_lo <= blk_hi) {   // empty when seq_lens < new tokens
+    fetch_ids(blk_hi);
+    load_block();
+  }
   bool wdone = false;   // slope bias: every P of this wave's remaining blocks is zero
   for (int blk = blk_hi; blk >= blk_lo; --blk) {
     const int j0 = blk * kBlkKeys;
+    if (blk > blk_lo) fetch_ids(blk - 1);   // page ids of the next load
     if constexpr (kKind == kBiasSlope) {
       // the remaining keys are <= j0 + 127: the bias of row r is at most the
       // one at distance max(0, P0 + r - (j0 + 127)); rows past the tile's
@@ -317,7 +328,7 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
     }
     stash_block(blk);
     __syncthreads();
-    if (blk > blk_lo) load_block(blk - 1);
+    if (blk > blk_lo) load_block();
     if (kKind == kBiasSlope && wdone) continue;
 
     // ---- per-wave bias table for this block: entry e <-> distance
