@@ -18,12 +18,12 @@
 //    32 PV MFMAs per wave;
 //  * K/V advance in 128-key blocks (8 pages). The workgroup copies a block's K
 //    rows (bank-swizzled) and its token-minor V^T pages, converted once to
-//    bf16, into LDS while the next block's bytes are already in flight in
+//    fp16, into LDS while the next block's bytes are already in flight in
 //    registers;
 //  * QK^T uses v_mfma_f32_16x16x128_f8f6f4 with the same lane mapping as
 //    decode: the key rows are permuted so that the S^T output lane of query row
 //    (l % 16) holds exactly the 32 keys PV consumes from it;
-//  * PV runs on v_mfma_f32_16x16x32_bf16 with P in bf16 (exact e4m3 V, 8-bit
+//  * PV runs on v_mfma_f32_16x16x32_f16 with P in fp16 (exact e4m3 V, 11-bit
 //    P mantissa, fp32 accumulation); a ones tile in the same MFMA stream
 //    accumulates the row sums of the rounded P, so the normaliser matches
 //    what PV summed;
@@ -34,10 +34,12 @@
 //  * blocks run from the diagonal outward (nearest keys first), so a row
 //    under a distance-decaying bias meets its largest scores first; the
 //    running max is lazy (raised only when a score passes it by more than 8,
-//    log2 units; bf16 P <= 2^8 keeps its relative precision), so O is rarely
+//    log2 units; fp16 P <= 2^8 keeps its relative precision), so O is rarely
 //    rescaled; and a wave whose every P in a block would be exactly zero
-//    (all exponents below -160: 2^-160 rounds to 0 in fp32 and bf16) skips
-//    that block's exp2 and PV, which leaves the result bit for bit unchanged;
+//    (every exponent argument at least 26 below the running max: fp16 rounds
+//    2^-26 to 0; with e4m3 P = 2^(x - m + 8), 19 below: e4m3 rounds 2^-11 to
+//    0) skips that block's exp2 and PV, which leaves the result bit for bit
+//    unchanged;
 //    with the slope bias (non-negative slopes) a wave stops altogether once
 //    a bound on every remaining score lies that far below the running max:
 //    |q . k| <= 448 * sum |q| (448 is the e4m3 maximum) and the bias only
@@ -81,7 +83,7 @@ __device__ __forceinline__ int kswz(int kidx) {
 
 struct __align__(16) PrefillSmem {
   uint4 k[kKBytes / 16];        // [128 keys][8 chunks of 16 B], chunk c at slot c ^ kswz(key)
-  uint4 v[2 * kVBytes / 16];    // bf16 V^T: [8 pages][2 halves][128 dims][8 tokens];
+  uint4 v[2 * kVBytes / 16];    // fp16 V^T: [8 pages][2 halves][128 dims][8 tokens];
                                 // fp8-P variant: e4m3 V^T [8 pages][128 dims][16 tokens]
                                 // in the first half
   float bias[kPW][kBiasWave];   // per wave: bias * log2(e) by distance, four copies
@@ -89,22 +91,22 @@ struct __align__(16) PrefillSmem {
   float qbound[kPW][32];        // slope bias: per wave and query row, 448 * sum |q|
 };
 
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ v8bf as_v8bf(uint4 x) { return __builtin_bit_cast(v8bf, x); }
+__device__ __forceinline__ v8h as_v8h(uint4 x) { return __builtin_bit_cast(v8h, x); }
 
-// Two e4m3 bytes of w (the low pair or the high pair) -> two bf16 in one
-// dword. Exact: an e4m3 value has at most 4 significant bits and its exponent
-// range fits bf16, so the fp32 value's upper half is the bf16 value.
+// Two e4m3 bytes of w (the low pair or the high pair) -> two fp16 in one
+// dword. Exact: every e4m3 value (4 significant bits, 2^-9 .. 448) is an
+// fp16 value.
 template <bool kHi>
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
-  const v2f f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHi);
-  return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHi));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const v2bf p = {(__bf16)lo, (__bf16)hi};
+// two fp32 -> fp16 (round to nearest even)
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const v2h p = {(_Float16)lo, (_Float16)hi};
   return __builtin_bit_cast(uint32_t, p);
 }
 
@@ -116,18 +118,26 @@ constexpr int kBiasNone = 0, kBiasSlope = 1, kBiasTable = 2;
 // the invariant log2(448) - 8 = 0.807).
 constexpr float kLazySlack = 0.75f;
 
-// Lazy-rescale slack of the bf16-P path (P <= 2^8), and the exponent gap
-// below the running max past which every P is exactly zero.
-constexpr float kLazyBf16 = 8.0f;
-constexpr float kZeroGap = 160.0f;
+// Lazy-rescale slack of the fp16-P path (P <= 2^8).
+constexpr float kLazyF16 = 8.0f;
 
-// P representations of PV: bf16 (default), one e4m3 term, two e4m3 terms.
-constexpr int kPBf16 = 0, kPFp8 = 1, kPFp8x2 = 2;
+// P representations of PV: fp16 (default), one e4m3 term, two e4m3 terms.
+constexpr int kPF16 = 0, kPFp8 = 1, kPFp8x2 = 2;
+
+// The exponent gap below the running max past which every P is exactly zero:
+// fp16 P = 2^(x - m) rounds to 0 below 2^-25 (half the smallest subnormal;
+// 2^-25 itself is a tie that goes to the even zero); e4m3 P = 2^(x - m + 8)
+// below 2^-10, and its second term, e4m3 of what the first left, is then
+// e4m3 of the same value. One more unit keeps the decision clear of the
+// rounding of x - m and of exp2's last bit.
+template <int kPMode>
+constexpr float zero_gap() { return kPMode == kPF16 ? 26.0f : 19.0f; }
 
 template <int kKind, int kPMode>
 __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blocks, int chunk, int nchunks) {
-  constexpr bool kP8 = kPMode != kPBf16;
+  constexpr bool kP8 = kPMode != kPF16;
+  constexpr float kGap = zero_gap<kPMode>();
   __shared__ PrefillSmem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -283,11 +293,11 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
           // e4m3 as stored: the 16 tokens of one dim of one page
           sm.v[pg * 128 + dim] = x;
         } else {
-          // tokens 0..7 -> half 0, 8..15 -> half 1, as bf16
-          sm.v[(pg * 2 + 0) * 128 + dim] = make_uint4(e4m3x2_to_bf16x2<false>(x.x), e4m3x2_to_bf16x2<true>(x.x),
-                                                       e4m3x2_to_bf16x2<false>(x.y), e4m3x2_to_bf16x2<true>(x.y));
-          sm.v[(pg * 2 + 1) * 128 + dim] = make_uint4(e4m3x2_to_bf16x2<false>(x.z), e4m3x2_to_bf16x2<true>(x.z),
-                                                       e4m3x2_to_bf16x2<false>(x.w), e4m3x2_to_bf16x2<true>(x.w));
+          // tokens 0..7 -> half 0, 8..15 -> half 1, as fp16
+          sm.v[(pg * 2 + 0) * 128 + dim] = make_uint4(e4m3x2_to_f16x2<false>(x.x), e4m3x2_to_f16x2<true>(x.x),
+                                                       e4m3x2_to_f16x2<false>(x.y), e4m3x2_to_f16x2<true>(x.y));
+          sm.v[(pg * 2 + 1) * 128 + dim] = make_uint4(e4m3x2_to_f16x2<false>(x.z), e4m3x2_to_f16x2<true>(x.z),
+                                                       e4m3x2_to_f16x2<false>(x.w), e4m3x2_to_f16x2<true>(x.w));
         }
       }
     }
@@ -313,7 +323,7 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
           const int r = cb * 16 + row;
           const int dmin = max(0, P0 + r - (j0 + kBlkKeys - 1));
           const float ub = fmaf(fold, sm.qbound[wave][r], round_bf16_finite(slope * -(float)dmin) * kLog2e);
-          ok = ok && (!head_ok || r >= ntok || ub < m_run[cb] - kZeroGap);
+          ok = ok && (!head_ok || r >= ntok || ub <= m_run[cb] - kGap);
         }
         wdone = __ballot(!ok) == 0;
       }
@@ -370,7 +380,7 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
       s[0][j] = mfma_16x16x128_e4m3(kop, qop[0], v4f{0.f, 0.f, 0.f, 0.f});
       s[1][j] = mfma_16x16x128_e4m3(kop, qop[1], v4f{0.f, 0.f, 0.f, 0.f});
     }
-    uint4 pk[2][4];     // P in bf16: pk[cb][kk] holds keys 8kk .. 8kk+7 of the lane group
+    uint4 pk[2][4];     // P in fp16: pk[cb][kk] holds keys 8kk .. 8kk+7 of the lane group
     v8i pk8[2];         // fp8-P variants: byte 4j + i of pk8[cb] is key 32*grp + 4j + i
     v8i pk8l[2];        // two-term variant: the second term, same layout
     const float scale = kBias ? 1.0f : fold;
@@ -414,11 +424,11 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
       bmax = wave_max_xor(bmax, 32);
       xmax[cb] = bmax * scale;
     }
-    // Every P of the block is 2^(x - m) with x <= xmax; when xmax lies more
-    // than kZeroGap below the running max in every row of the wave, all of
-    // them round to zero and PV would add exact zeros: skip the block. (With
-    // no key seen yet, m = -inf and a finite xmax is live.)
-    if (!__ballot(xmax[0] > m_run[0] - kZeroGap || xmax[1] > m_run[1] - kZeroGap)) continue;
+    // Every P of the block is 2^(x - m) (times 2^8 for e4m3 P) with x <= xmax;
+    // when xmax lies kGap or more below the running max in every row of the
+    // wave, all of them round to zero and PV would add exact zeros: skip the
+    // block. (With no key seen yet, m = -inf and a finite xmax is live.)
+    if (!__ballot(xmax[0] > m_run[0] - kGap || xmax[1] > m_run[1] - kGap)) continue;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       if constexpr (kP8) {
@@ -451,8 +461,8 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
         continue;
       }
       // lazy max: raised (to the block max) only when a score passes it by
-      // more than kLazyBf16, so P <= 2^8
-      const bool raise = xmax[cb] > m_run[cb] + kLazyBf16;
+      // more than kLazyF16, so P <= 2^8
+      const bool raise = xmax[cb] > m_run[cb] + kLazyF16;
       const float alpha = raise ? __builtin_amdgcn_exp2f(m_run[cb] - xmax[cb]) : 1.0f;   // 0 from -inf
       if (raise) m_run[cb] = xmax[cb];
       const float m_use = m_run[cb] == -INFINITY ? 0.0f : m_run[cb];
@@ -464,8 +474,8 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           pv[e] = __builtin_amdgcn_exp2f(fmaf(s[cb][2 * kk + (e >> 2)][e & 3], scale, -m_use));
-        pk[cb][kk] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                                pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
+        pk[cb][kk] = make_uint4(pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]),
+                                pack_f16x2(pv[4], pv[5]), pack_f16x2(pv[6], pv[7]));
       }
       if (__ballot(alpha != 1.0f)) {
 #pragma unroll
@@ -505,23 +515,23 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
       }
       continue;
     }
-    // ---- O^T += V^T P^T (bf16 MFMA, 32 keys per step) for both column
+    // ---- O^T += V^T P^T (fp16 MFMA, 32 keys per step) for both column
     // blocks from one V^T operand read; tile t covers dims 16t .. 16t+15,
     // step kk keys 8kk .. 8kk+7 of every lane group. A ones tile accumulates
     // the row sums of the same rounded P.
-    const v8bf ones = as_v8bf(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+    const v8h ones = as_v8h(make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const v8bf p0 = as_v8bf(pk[0][kk]), p1 = as_v8bf(pk[1][kk]);
+      const v8h p0 = as_v8h(pk[0][kk]), p1 = as_v8h(pk[1][kk]);
       const uint4 *vrow = sm.v + ((2 * grp + (kk >> 1)) * 2 + (kk & 1)) * 128 + row;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const v8bf va = as_v8bf(vrow[16 * t]);
-        o[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, p0, o[0][t], 0, 0, 0);
-        o[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, p1, o[1][t], 0, 0, 0);
+        const v8h va = as_v8h(vrow[16 * t]);
+        o[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, p0, o[0][t], 0, 0, 0);
+        o[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, p1, o[1][t], 0, 0, 0);
       }
-      ol[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, p0, ol[0], 0, 0, 0);
-      ol[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, p1, ol[1], 0, 0, 0);
+      ol[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, p0, ol[0], 0, 0, 0);
+      ol[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, p1, ol[1], 0, 0, 0);
     }
   }
 
@@ -566,7 +576,7 @@ hipError_t launch_prefill_e4m3(const PrefillE4M3Launch &a, hipStream_t s) {
   } while (0)
   if (a.p_mode == 1) KVQ_PREFILL_KINDS(kPFp8);
   else if (a.p_mode == 2) KVQ_PREFILL_KINDS(kPFp8x2);
-  else KVQ_PREFILL_KINDS(kPBf16);
+  else KVQ_PREFILL_KINDS(kPF16);
 #undef KVQ_PREFILL_KINDS
 #undef KVQ_PREFILL_LAUNCH
   return hipGetLastError();

@@ -141,10 +141,14 @@ enum {
      hi)) on fp8 MFMA, with the same lazy running max (slack 0.75) and a
      normaliser summed from the same two terms ([PR54705] evidence "Tier 0"
      for the 2^8 pre-scale and its log2(448) - 8 bound). About 8 significant
-     bits per weight, like the default bf16 P; an alternative P path kept for
-     its measured comparison with the default (two fp8 MFMAs cost what one
-     bf16 MFMA does, and the split costs vector instructions). At most one of
-     the two flags may be set. */
+     bits per weight (the default fp16 P keeps 11); the fp8-PV path, within
+     the default tolerance, kept beside the default for its measured
+     comparison: blocks whose every P rounds to zero are skipped, and e4m3
+     P = 2^(x - m + 8) reaches zero 19 log2 units below the running max
+     against 26 for fp16 P, so with a decaying bias this path skips more and
+     can be the faster one; without a bias it is the slower one (two fp8
+     MFMAs cost what one fp16 MFMA does, and the split costs vector
+     instructions). At most one of the two flags may be set. */
   KVQ_FLAG_PREFILL_FP8_P2 = 2u
 };
 

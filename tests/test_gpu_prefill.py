@@ -182,7 +182,7 @@ def slope_table(slopes, extent):
     return torch.from_numpy(prod).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("pmode", ["bf16", "fp8_p", "fp8_p2"])
+@pytest.mark.parametrize("pmode", ["f16", "fp8_p", "fp8_p2"])
 @pytest.mark.parametrize("which", ["small", "full"])
 def test_prefill_slope_early_stop_is_exact(which, pmode):
     """With the slope bias a wave stops once a bound puts every remaining
@@ -199,7 +199,7 @@ def test_prefill_slope_early_stop_is_exact(which, pmode):
     dc = DeviceCase(c)
     s = dc.calibrate()
     dc.store_all(s)
-    mode = {} if pmode == "bf16" else {pmode: True}
+    mode = {} if pmode == "f16" else {pmode: True}
     a = dc.prefill(s, **mode)
     tab = slope_table(c.slopes, c.max_seq_len).cuda()
     b = kvq.prefill(dc.cache, dc.q, dc.cu_q_lens, c.max_q_len, dc.block_table, dc.seq_lens,
