@@ -157,9 +157,16 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
   const int u = pair / nchunks;
   const int tile = (pair - u * nchunks) * chunk + slot % chunk;
   if (u >= units || tile >= tiles) return;
+  // Units are numbered KV head outermost, the last KV head first: under the
+  // slope bias of the ALiBi family the slopes fall with the head index, so
+  // the last heads reach farthest back before their probabilities vanish and
+  // cost the most; dispatching them first leaves the cheap units for the end
+  // (otherwise the last costly workgroups started late set the kernel's end).
+  // Without a slope bias every unit costs about the same and the order does
+  // not matter.
   const int hb = u % head_blocks;
-  const int g = (u / head_blocks) % a.hkv;
-  const int b = u / (head_blocks * a.hkv);
+  const int b = (u / head_blocks) % a.batch;
+  const int g = a.hkv - 1 - u / (head_blocks * a.batch);
   const int q0 = a.cu_q_lens[b];
   const int lq = a.cu_q_lens[b + 1] - q0;
   if (tile * kTileTok >= lq) return;
