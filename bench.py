@@ -611,7 +611,8 @@ def prefill_rows(torch, kvq):
     # the slope bias (the workload's main row): blocks whose every probability
     # is exactly zero are skipped, so the flops are nominal
     r = timed_row(torch, run(slopes=slopes), "mfma", fl, PREFILL_MIXED_PEAK_TFLOPS, "TFLOP/s", per=1, sha=sha,
-                  roof_extra=dict(mix, flops_kind="nominal: every causal pair, also skipped exact zeros"),
+                  roof_extra=dict(mix, flops_kind="nominal: every causal pair, also skipped exact zeros; frac above 1 "
+                                                    "means the skipped work outweighs the shortfall from peak"),
                   **shape)
     r["nominal_pct_of_fp8_peak"] = round(100 * r["roofline"]["achieved"] / FP8_PEAK_TFLOPS, 2)
     if "prefill_e4m3_kernel<1, 0>" in issue:
