@@ -208,3 +208,41 @@ def test_prefill_slope_early_stop_is_exact(which, pmode):
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(a.float()))
     assert torch.equal(a, b)
+
+
+def far_live_case():
+    """A key that outscores every other by far, planted 3,800+ positions behind
+    the new tokens: under a slope of 0.05 per position the blocks between it
+    and the diagonal hold only probabilities that round to zero and are
+    skipped, and the planted key's block, far out, must not be. Every query
+    has +5 on dim 0 and the planted key is 3,000 e_0."""
+    c = make_attn_case("farlive", 91, [4096, 700], [64, 40], 8, 1, 128,
+                       slopes=np.full(8, 0.05, dtype=np.float32))
+    q = c.q.float()
+    q[:, :, 0] += 5.0
+    c.q = q.to(torch.bfloat16)
+    k = c.k.float()
+    planted = int(np.nonzero((c.seq_of_token == 0) & (c.pos_of_token == 200))[0][0])
+    k[planted] = 0.0
+    k[planted, 0, 0] = 3000.0
+    c.k = k.to(torch.bfloat16)
+    return c
+
+
+@pytest.mark.parametrize("pmode", ["f16", "fp8_p2"])
+def test_prefill_far_live_block_after_skipped_blocks(pmode):
+    """The block holding the planted key is needed for PV although many blocks
+    before it were skipped (and the slope path's early stop must not fire
+    before it). Checked against the oracle, and bit for bit against the
+    learned-table path given the same biases."""
+    c = far_live_case()
+    mode = {} if pmode == "f16" else {pmode: True}
+    dc, out, ref = run_case(c, **mode)
+    print(check_attention(out, ref, "far live block %s" % pmode))
+    s = dc.calibrate()
+    tab = slope_table(c.slopes, c.max_seq_len).cuda()
+    b = kvq.prefill(dc.cache, dc.q, dc.cu_q_lens, c.max_q_len, dc.block_table, dc.seq_lens,
+                    c.max_seq_len, c.softmax_scale, s["q"], s["k"], s["v"], c.window, None,
+                    rel_bias=tab, **mode)
+    torch.cuda.synchronize()
+    assert torch.equal(out, b)
