@@ -242,14 +242,16 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
   // ---- block loader: thread chunk q in [0, 2048): q < 1024 -> K, else V^T;
   // 128 chunks (2 KB) per page. Pages past the sequence end are clamped.
   // Chunk c of a thread lies in block page (wave / 2) + 4 (c & 1), so a wave
-  // needs two page ids per block; they are read a block ahead (fetch_ids),
-  // which keeps the block-table round trip out of the loads' issue.
+  // needs two page ids per block; they are read two blocks ahead of their
+  // load (fetch_ids), which keeps the block-table round trip out of the
+  // loads' issue.
   static_assert(kLoadChunks == 4 && 64 * kPW == 512, "chunk -> page mapping");
   uint4 pre[kLoadChunks];
-  int ids[2];
-  auto fetch_ids = [&](int blk) {
+  int ids[2];        // page ids of the next load
+  int ids_n[2];      // and of the load after it
+  auto fetch_ids = [&](int blk, int (&dst)[2]) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) ids[h] = bt[min(blk * 8 + (wave >> 1) + 4 * h, page_last)];
+    for (int h = 0; h < 2; ++h) dst[h] = bt[min(blk * 8 + (wave >> 1) + 4 * h, page_last)];
   };
   auto load_block = [&]() {
 #pragma unroll
@@ -312,13 +314,14 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
 
   const float fold = a.fold_log2;
   if (blk_lo <= blk_hi) {   // empty when seq_lens < new tokens
-    fetch_ids(blk_hi);
+    fetch_ids(blk_hi, ids);
     load_block();
+    if (blk_hi > blk_lo) fetch_ids(blk_hi - 1, ids);
   }
   bool wdone = false;   // slope bias: every P of this wave's remaining blocks is zero
   for (int blk = blk_hi; blk >= blk_lo; --blk) {
     const int j0 = blk * kBlkKeys;
-    if (blk > blk_lo) fetch_ids(blk - 1);   // page ids of the next load
+    if (blk - 1 > blk_lo) fetch_ids(blk - 2, ids_n);   // page ids of the load after next
     if constexpr (kKind == kBiasSlope) {
       // the remaining keys are <= j0 + 127: the bias of row r is at most the
       // one at distance max(0, P0 + r - (j0 + 127)); rows past the tile's
@@ -345,9 +348,52 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
     }
     stash_block(blk);
     __syncthreads();
-    if (blk > blk_lo) load_block();
+    if (blk > blk_lo) {
+      load_block();
+#pragma unroll
+      for (int h = 0; h < 2; ++h) ids[h] = ids_n[h];
+    }
     if (kKind == kBiasSlope && wdone) continue;
 
+    const bool edge = (j0 + kBlkKeys - 1 > P0) || (a.window > 0 && j0 < khi - a.window);
+    // ---- S^T = K Q^T for both column blocks, sharing every K operand read.
+    // Lane (row, grp) gets keys kidx = 32*grp + 16*(j/4) + 4*(j%4) + i of
+    // query row cb*16 + row.
+    v4f s[2][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kidx = 32 * (row >> 2) + 16 * (j >> 2) + 4 * (j & 3) + (row & 3);
+      const int c0 = 2 * grp;
+      const uint4 x0 = sm.k[kidx * 8 + (c0 ^ kswz(kidx))];
+      const uint4 x1 = sm.k[kidx * 8 + ((c0 + 1) ^ kswz(kidx))];
+      const v8i kop = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      s[0][j] = mfma_16x16x128_e4m3(kop, qop[0], v4f{0.f, 0.f, 0.f, 0.f});
+      s[1][j] = mfma_16x16x128_e4m3(kop, qop[1], v4f{0.f, 0.f, 0.f, 0.f});
+    }
+    if constexpr (kKind == kBiasSlope) {
+      // Cheap dead-block test: the bias falls with distance, so no exponent
+      // argument of row r exceeds fold * (the row's largest raw score) + the
+      // bias at the row's nearest key of the block; when that lies kGap or
+      // more below the running max in every row of the wave with a query
+      // (rows past the tile's tokens are not written), every P of the block
+      // is zero: skip it before the bias table and its lookups. (fmaf is
+      // monotone in both arguments, so the bound holds after rounding.)
+      bool live = false;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        float smax = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          smax = fmaxf(smax, fmaxf(fmaxf(s[cb][j][0], s[cb][j][1]), fmaxf(s[cb][j][2], s[cb][j][3])));
+        smax = wave_max_xor(smax, 16);
+        smax = wave_max_xor(smax, 32);
+        const int r = cb * 16 + row;
+        const int dmin = max(0, P0 + r - (j0 + kBlkKeys - 1));
+        const float ub = fmaf(fold, smax, round_bf16_finite(slope * -(float)dmin) * kLog2e);
+        live = live || (head_ok && r < ntok && ub > m_run[cb] - kGap);
+      }
+      if (!__ballot(live)) continue;
+    }
     // ---- per-wave bias table for this block: entry e <-> distance
     // d = (P0 - j0) + e - 127, value bf16(slope * -d) or T[min(d, E - 1)],
     // times log2(e). With the learned table, a block whose nearest key is at
@@ -372,21 +418,6 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
-    const bool edge = (j0 + kBlkKeys - 1 > P0) || (a.window > 0 && j0 < khi - a.window);
-    // ---- S^T = K Q^T for both column blocks, sharing every K operand read.
-    // Lane (row, grp) gets keys kidx = 32*grp + 16*(j/4) + 4*(j%4) + i of
-    // query row cb*16 + row.
-    v4f s[2][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kidx = 32 * (row >> 2) + 16 * (j >> 2) + 4 * (j & 3) + (row & 3);
-      const int c0 = 2 * grp;
-      const uint4 x0 = sm.k[kidx * 8 + (c0 ^ kswz(kidx))];
-      const uint4 x1 = sm.k[kidx * 8 + ((c0 + 1) ^ kswz(kidx))];
-      const v8i kop = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      s[0][j] = mfma_16x16x128_e4m3(kop, qop[0], v4f{0.f, 0.f, 0.f, 0.f});
-      s[1][j] = mfma_16x16x128_e4m3(kop, qop[1], v4f{0.f, 0.f, 0.f, 0.f});
-    }
     uint4 pk[2][4];     // P in fp16: pk[cb][kk] holds keys 8kk .. 8kk+7 of the lane group
     v8i pk8[2];         // fp8-P variants: byte 4j + i of pk8[cb] is key 32*grp + 4j + i
     v8i pk8l[2];        // two-term variant: the second term, same layout
