@@ -87,7 +87,7 @@ struct __align__(16) PrefillSmem {
                                 // fp8-P variant: e4m3 V^T [8 pages][128 dims][16 tokens]
                                 // in the first half
   float bias[kPW][kBiasWave];   // per wave: bias * log2(e) by distance, four copies
-  int done[2][kPW];             // slope bias: waves whose remaining blocks are all zero P
+  __attribute__((aligned(16))) int done[2][kPW];   // slope bias: waves whose remaining blocks are all zero P
   float qbound[kPW][32];        // slope bias: per wave and query row, 448 * sum |q|
 };
 
@@ -341,10 +341,12 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
     }
     __syncthreads();                  // everyone is done reading the previous block
     if constexpr (kKind == kBiasSlope) {
-      bool all = true;
-#pragma unroll
-      for (int w = 0; w < kPW; ++w) all = all && sm.done[blk & 1][w] != 0;
-      if (all) break;                 // uniform: every wave reads the same flags
+      // the eight flags (0 or 1) in two 16-byte reads: a short-circuit loop
+      // would wait for each read before issuing the next
+      static_assert(kPW == 8, "two uint4 of flags");
+      const uint4 f0 = *(const uint4 *)&sm.done[blk & 1][0];
+      const uint4 f1 = *(const uint4 *)&sm.done[blk & 1][4];
+      if ((f0.x & f0.y & f0.z & f0.w & f1.x & f1.y & f1.z & f1.w) != 0) break;   // uniform
     }
     stash_block(blk);
     __syncthreads();
