@@ -47,8 +47,8 @@ WARM = 5             # warm-up calls per row
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--skip-extras", action="store_true", help="only the headline step")
     ap.add_argument("--skip-cpu", action="store_true", help="no CPU oracle baseline")
     ap.add_argument("--copy-probe", action="store_true",

@@ -152,25 +152,39 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 
   // Fused append: the current token (position L - 1, in the last block) is
   // quantized with the store's quantizer and written into its page by the
-  // wave that reads that block, before it loads the block. With several
-  // query tiles each tile's workgroup writes the same bytes.
+  // wave that reads that block. Its bf16 K/V and page id are requested here;
+  // the bytes are written once the wave's first block has its loads in
+  // flight (so the wave starts as early as the others), or before those
+  // loads when that first block is the last one. With several query tiles
+  // each tile's workgroup writes the same bytes.
   const int blk_last = nblk - 1;
+  const int blk_first = blk_begin + wave;   // this wave's first block
   const bool appender = a.k_new != nullptr && L > 0 && blk_last >= blk_begin && blk_last < blk_end &&
                         wave == (blk_last - blk_begin) % W;
-  if (appender && lane < D / 8) {
-    const int pos = L - 1;
-    const size_t base = (size_t)bt[pos >> 4] * page_stride + g_off;
+  const bool app_lane = appender && lane < D / 8;
+  uint4 k_tok = make_uint4(0u, 0u, 0u, 0u), v_tok = k_tok;
+  int app_page = 0;
+  if (app_lane) {
     const size_t src = ((size_t)b * a.hkv + g) * D + 8 * lane;
-    const uint2 kq = quant8_e4m3(*(const uint4 *)(a.k_new + src), a.k_inv);
-    const uint2 vq = quant8_e4m3(*(const uint4 *)(a.v_new + src), a.v_inv);
-    *(uint2 *)(a.kc_w + base + (size_t)(pos & 15) * D + 8 * lane) = kq;
-    uint8_t *vdst = a.vc_w + base + (pos & 15) + 16 * (8 * lane);   // token-minor: dim d at 16 d
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      vdst[16 * i] = (uint8_t)(vq.x >> (8 * i));
-      vdst[16 * (4 + i)] = (uint8_t)(vq.y >> (8 * i));
-    }
+    k_tok = *(const uint4 *)(a.k_new + src);
+    v_tok = *(const uint4 *)(a.v_new + src);
+    app_page = bt[(L - 1) >> 4];
   }
+  auto append = [&]() {
+    if (app_lane) {
+      const int pos = L - 1;
+      const size_t base = (size_t)app_page * page_stride + g_off;
+      const uint2 kq = quant8_e4m3(k_tok, a.k_inv);
+      const uint2 vq = quant8_e4m3(v_tok, a.v_inv);
+      *(uint2 *)(a.kc_w + base + (size_t)(pos & 15) * D + 8 * lane) = kq;
+      uint8_t *vdst = a.vc_w + base + (pos & 15) + 16 * (8 * lane);   // token-minor: dim d at 16 d
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vdst[16 * i] = (uint8_t)(vq.x >> (8 * i));
+        vdst[16 * (4 + i)] = (uint8_t)(vq.y >> (8 * i));
+      }
+    }
+  };
 
   // head_dim 128: lane l holds the physical page of page (l & 7) of the next
   // block, clamped to the sequence's last page.
@@ -182,6 +196,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 
   for (int blk = blk_begin + wave; blk < blk_end; blk += W) {
     if (appender && blk == blk_last) {
+      if (blk == blk_first) append();
       // the appended bytes are in memory before this block's loads
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -229,6 +244,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       pid_next = bt[min(page_lo + nblk_next * 8 + (lane & 7), page_hi - 1)];
       // keep all of the block's loads ahead of the LDS writes that wait on them
       __builtin_amdgcn_sched_barrier(0);
+      if (blk == blk_first && blk != blk_last) append();
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int slot = (lane & 7) ^ ((lane >> 3) & 3) ^ (4 * ((i >> 2) & 1));
@@ -268,6 +284,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         const v4u x1 = __builtin_nontemporal_load((const v4u *)(vb1 + 256 * t));
         vop[t] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
       }
+      if (blk == blk_first && blk != blk_last) append();
     }
 
     // ---- S^T = K Q^T: lane holds keys (vp0 + j/4, token 4*(j%4) + i) of its query row
