@@ -101,9 +101,12 @@ kvq::DecodePlan plan_decode(const kvq_cache *c, int32_t num_seqs, int32_t max_se
   } else {
     splits = splits_for(pl.waves);
     // few (sequence, KV head) units over long sequences: fewer waves per
-    // workgroup and more splits, so that the workgroups still cover every
-    // compute unit (short sequences keep their single split: no combine)
-    while (nblk > 8 && pl.waves > 1 && units * splits < current_cu_count()) {
+    // workgroup and more splits while the workgroups cover less than half of
+    // the compute units (short sequences keep their single split: no
+    // combine). Half is enough: the combine's cost grows with the split
+    // count (one sequence over 65,536 keys on 2 KV heads: 64 splits of 8
+    // waves 15.1 us per call, 128 of 4 waves 15.8, 256 of 2 waves 24.1)
+    while (nblk > 8 && pl.waves > 1 && 2 * units * splits < current_cu_count()) {
       const int64_t s2 = splits_for(pl.waves / 2);
       if (s2 <= splits) break;
       pl.waves /= 2;
