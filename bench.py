@@ -596,7 +596,13 @@ def prefill_rows(torch, kvq):
     mix = {"dtype": "fp8 QK^T + fp16 PV", "peak_note": "half the flops at each MFMA rate"}
     issue = issue_record() or {}
 
+    # the slope-bias calls' key-norm workspace, allocated once
+    pws = torch.empty(max(kvq.prefill_workspace_bytes(cache, c.batch, c.max_seq_len, c.num_q_heads, slopes=slopes),
+                          1), dtype=torch.uint8, device=dev)
+
     def run(**kw):
+        if kw.get("slopes") is not None and kw.get("use_workspace", True):
+            kw["workspace"] = pws
         return lambda i: kvq.prefill(cache, q, cu, c.max_q_len, bt, sl, c.max_seq_len, c.softmax_scale, sc["q"],
                                      sc["k"], sc["v"], out=out, **kw)
     shape = {"batch": c.batch, "new_tokens": int(c.q_lens[0]), "context": c.max_seq_len}
@@ -618,6 +624,11 @@ def prefill_rows(torch, kvq):
     if "prefill_e4m3_kernel<1, 0>" in issue:
         r.update(issue["prefill_e4m3_kernel<1, 0>"])
     rows["chunked_prefill"] = r
+    # the same call without the key-norm workspace: the early stop uses the
+    # looser 448 * sum |q| bound (same output)
+    r = timed_row(torch, run(slopes=slopes, use_workspace=False), "mfma", fl, PREFILL_MIXED_PEAK_TFLOPS, "TFLOP/s",
+                  per=1, sha=sha, roof_extra=dict(mix, flops_kind="nominal"), **shape)
+    rows["chunked_prefill_no_key_norms"] = r
     # the same prefill with a learned relative-bias table of 1,024 entries
     rel = torch.from_numpy(rel_bias_table(np.random.default_rng(6), c.num_q_heads, 1024)).to(torch.bfloat16).to(dev)
     r = timed_row(torch, run(rel_bias=rel), "mfma", fl, PREFILL_MIXED_PEAK_TFLOPS, "TFLOP/s", per=1, sha=sha,

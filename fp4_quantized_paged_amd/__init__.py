@@ -53,7 +53,7 @@ FLAG_PREFILL_FP8_P2 = 2
 
 
 _lib = None
-ABI_VERSION = 6   # KVQ_ABI_VERSION of include/kvq.h
+ABI_VERSION = 7   # KVQ_ABI_VERSION of include/kvq.h
 
 _SIGNATURES = {
     "kvq_abi_version": (ctypes.c_int, []),
@@ -89,6 +89,8 @@ _SIGNATURES = {
                                                      ctypes.c_int32, ctypes.c_int32,
                                                      ctypes.POINTER(AttnParams), ctypes.c_void_p,
                                                      ctypes.c_void_p]),
+    "kvq_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), ctypes.c_int32,
+                                                      ctypes.c_int32, ctypes.POINTER(AttnParams)]),
     "kvq_paged_attn_prefill": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                               ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
@@ -397,17 +399,29 @@ def decode_noalloc(cache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: 
     return out
 
 
+def prefill_workspace_bytes(cache, num_seqs: int, max_seq_len: int, num_q_heads: int,
+                            slopes: Optional[torch.Tensor] = None, softmax_scale: float = 1.0) -> int:
+    """kvq_prefill_workspace_bytes: bytes of the optional per-block key-norm
+    workspace of a slope-bias prefill (0 when it does not apply)."""
+    p = _params(num_q_heads, softmax_scale, 1.0, 1.0, 1.0, 0, slopes, 0)
+    return int(lib().kvq_prefill_workspace_bytes(ctypes.byref(cache.desc), int(num_seqs), int(max_seq_len),
+                                                 ctypes.byref(p)))
+
+
 def prefill(cache, q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,
             block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
             softmax_scale: float, q_scale: float = 1.0, k_scale: float = 1.0,
             v_scale: float = 1.0, window: int = 0, slopes: Optional[torch.Tensor] = None,
             out: Optional[torch.Tensor] = None, rel_bias: Optional[torch.Tensor] = None,
-            fp8_p: bool = False, fp8_p2: bool = False) -> torch.Tensor:
+            fp8_p: bool = False, fp8_p2: bool = False,
+            workspace: Optional[torch.Tensor] = None, use_workspace: bool = True) -> torch.Tensor:
     """kvq_paged_attn_prefill. q bf16 [sumQ, Hq, Dqk] -> out bf16 [sumQ, Hq, Dv].
     rel_bias: learned relative-bias table, bf16 [Hq, extent]. fp8_p: the
     single-term e4m3 P speed variant (KVQ_FLAG_PREFILL_FP8_P); fp8_p2: the
-    two-term e4m3 P path (KVQ_FLAG_PREFILL_FP8_P2)."""
-    _need_cuda(q, cu_q_lens, block_table, seq_lens, slopes, rel_bias, out)
+    two-term e4m3 P path (KVQ_FLAG_PREFILL_FP8_P2). With slopes, the
+    per-block key-norm workspace is used (allocated here when not passed)
+    unless use_workspace is False; the output is the same either way."""
+    _need_cuda(q, cu_q_lens, block_table, seq_lens, slopes, rel_bias, out, workspace)
     dqk, dv = _head_dims(cache)
     if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous() or q.shape[2] != dqk:
         raise ValueError("q must be contiguous bf16 [sumQ, Hq, %d], got %s %s" % (dqk, q.dtype, tuple(q.shape)))
@@ -425,9 +439,17 @@ def prefill(cache, q: torch.Tensor, cu_q_lens: torch.Tensor, max_q_len: int,
     _check_out(out, (total_q, Hq, dv))
     p = _params(Hq, softmax_scale, q_scale, k_scale, v_scale, window, slopes, 0, rel_bias,
                 (FLAG_PREFILL_FP8_P if fp8_p else 0) | (FLAG_PREFILL_FP8_P2 if fp8_p2 else 0))
+    ws_bytes = 0
+    if use_workspace:
+        need = int(lib().kvq_prefill_workspace_bytes(ctypes.byref(d), B, int(max_seq_len), ctypes.byref(p)))
+        if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    else:
+        workspace = None
     st = lib().kvq_paged_attn_prefill(ctypes.byref(d), _ptr(q), _ptr(cu_q_lens), total_q,
                                       int(max_q_len), _ptr(block_table), block_table.stride(0),
                                       _ptr(seq_lens), int(seq_lens.shape[0]), int(max_seq_len),
-                                      ctypes.byref(p), _ptr(out), None, 0, _stream())
+                                      ctypes.byref(p), _ptr(out), _ptr(workspace), ws_bytes, _stream())
     _check(st, "kvq_paged_attn_prefill")
     return out

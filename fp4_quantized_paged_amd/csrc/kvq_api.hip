@@ -155,6 +155,14 @@ kvq::MlaPlan plan_mla(int32_t num_seqs, int32_t max_seq_len, const kvq_attn_para
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
+// Per-block key norms of the slope-bias prefill: one float per (sequence,
+// KV head, 128-key block).
+size_t prefill_knorm_bytes(const kvq_cache *c, int32_t num_seqs, int32_t max_seq_len, const kvq_attn_params *p) {
+  if (c->format != KVQ_FMT_E4M3 || p->alibi_slopes == nullptr || num_seqs <= 0 || max_seq_len <= 0) return 0;
+  return static_cast<size_t>(num_seqs) * c->num_kv_heads * ((static_cast<size_t>(max_seq_len) + 127) / 128) *
+         sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -414,13 +422,18 @@ int kvq_paged_attn_decode_append(const kvq_cache *cache, const void *q, const vo
                      max_seq_len, params, out, workspace, workspace_bytes, stream);
 }
 
+size_t kvq_prefill_workspace_bytes(const kvq_cache *cache, int32_t num_seqs, int32_t max_seq_len,
+                                   const kvq_attn_params *params) {
+  if (check_cache(cache) != KVQ_OK || check_params(cache, params) != KVQ_OK || num_seqs < 0 || max_seq_len < 0)
+    return 0;
+  return prefill_knorm_bytes(cache, num_seqs, max_seq_len, params);
+}
+
 int kvq_paged_attn_prefill(const kvq_cache *cache, const void *q, const int32_t *cu_q_lens, int64_t total_q,
                            int32_t max_q_len, const int32_t *block_table, int64_t block_table_stride,
                            const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
                            const kvq_attn_params *params, void *out, void *workspace,
                            size_t workspace_bytes, kvq_stream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   int st = check_cache(cache);
   if (st != KVQ_OK) return st;
   if (cache->format == KVQ_FMT_E4M3 && cache->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
@@ -472,6 +485,12 @@ int kvq_paged_attn_prefill(const kvq_cache *cache, const void *q, const int32_t 
   a.q_inv = 1.0f / params->q_scale;
   a.fold_log2 = params->softmax_scale * params->q_scale * params->k_scale * 1.4426950408889634f;
   a.v_scale = params->v_scale;
+  const size_t knorm_bytes = prefill_knorm_bytes(cache, num_seqs, max_seq_len, params);
+  if (knorm_bytes > 0 && workspace != nullptr && workspace_bytes >= knorm_bytes &&
+      (reinterpret_cast<uintptr_t>(workspace) & 3) == 0) {
+    a.knorm = static_cast<float *>(workspace);
+    a.knorm_blocks = static_cast<int>((static_cast<int64_t>(max_seq_len) + 127) / 128);
+  }
   return hip_status(kvq::launch_prefill_e4m3(a, reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -95,9 +95,14 @@ struct PrefillE4M3Launch {
   int rel_extent;
   uint16_t *out;
   int batch, hq, hkv, d, window, max_q_len;
-  int p_mode;                  // P of PV: 0 bf16; 1 one e4m3 term, 2 two e4m3 terms (both
+  int p_mode;                  // P of PV: 0 fp16; 1 one e4m3 term, 2 two e4m3 terms (both
                                // with a lazy rescale of slack 0.75, on fp8 MFMA)
   float q_inv, fold_log2, v_scale;
+  // slope bias only (nullptr: not used): per (sequence, KV head, 128-key
+  // block) the largest Euclidean norm of the block's key codes,
+  // [batch][hkv][knorm_blocks], written by a launch before the prefill's
+  int knorm_blocks;
+  float *knorm;
 };
 hipError_t launch_prefill_e4m3(const PrefillE4M3Launch &a, hipStream_t s);
 

@@ -62,6 +62,7 @@ constexpr int kD = 128;           // head dim
 constexpr int kKBytes = kBlkKeys * kD;          // 16 KB of K rows per block
 constexpr int kVBytes = kBlkKeys * kD;          // 16 KB of V^T per block
 constexpr int kBiasN = 160;                     // bias table entries (distances) of a block
+constexpr int kMaxPM = 1024;                    // slope bias: key-norm prefix maxima held in LDS
 constexpr int kBiasWave = 736;                  // four copies per wave, one per lane group
 
 // Lane group g reads its own copy of the wave's bias table, starting at entry
@@ -89,6 +90,9 @@ struct __align__(16) PrefillSmem {
   float bias[kPW][kBiasWave];   // per wave: bias * log2(e) by distance, four copies
   __attribute__((aligned(16))) int done[2][kPW];   // slope bias: waves whose remaining blocks are all zero P
   float qbound[kPW][32];        // slope bias: per wave and query row, 448 * sum |q|
+  float qnorm[kPW][32];         // slope bias: per wave and query row, |q| (Euclidean, codes)
+  float pm[kMaxPM];             // slope bias: largest key norm of blocks blk_lo .. blk_lo + i
+  float pmw[kPW];               // per-wave maxima of the prefix scan
 };
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -208,21 +212,55 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
   if constexpr (kKind == kBiasSlope) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      float acc = 0.0f;
+      float acc = 0.0f, acc2 = 0.0f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(qop[cb][c], false);
         const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(qop[cb][c], true);
         acc += (fabsf(lo.x) + fabsf(lo.y)) + (fabsf(hi.x) + fabsf(hi.y));
+        acc2 += (lo.x * lo.x + lo.y * lo.y) + (hi.x * hi.x + hi.y * hi.y);
       }
       acc += __shfl_xor(acc, 16, 64);
       acc += __shfl_xor(acc, 32, 64);
-      if (grp == 0) sm.qbound[wave][cb * 16 + row] = acc * (448.0f * 1.001f);
+      acc2 += __shfl_xor(acc2, 16, 64);
+      acc2 += __shfl_xor(acc2, 32, 64);
+      if (grp == 0) {
+        sm.qbound[wave][cb * 16 + row] = acc * (448.0f * 1.001f);
+        sm.qnorm[wave][cb * 16 + row] = sqrtf(acc2) * 1.001f;
+      }
     }
     // read back by every lane group of this wave
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  // Slope bias with key norms: pm[i] = the largest key-code norm of blocks
+  // blk_lo .. blk_lo + i (an inclusive prefix max: thread t takes blocks 2t
+  // and 2t + 1, a wave scan, then the maxima of the earlier waves). A wave at
+  // block blk then bounds every remaining raw score of row r by
+  // |q_r| * pm[blk - blk_lo] (Cauchy-Schwarz over the codes).
+  const bool use_pm = kKind == kBiasSlope && a.knorm != nullptr && blk_lo <= blk_hi &&
+                      blk_hi - blk_lo + 1 <= kMaxPM && blk_hi < a.knorm_blocks;
+  if (use_pm) {   // uniform over the workgroup
+    const float *kn = a.knorm + ((size_t)b * a.hkv + g) * a.knorm_blocks + blk_lo;
+    const int n = blk_hi - blk_lo + 1;
+    const float v0 = 2 * tid < n ? kn[2 * tid] : 0.0f;
+    const float v1 = 2 * tid + 1 < n ? fmaxf(v0, kn[2 * tid + 1]) : v0;
+    float x = v1;   // inclusive scan over the wave's lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float y = __shfl_up(x, d, 64);
+      if (lane >= d) x = fmaxf(x, y);
+    }
+    float before = __shfl_up(x, 1, 64);   // lanes below this one
+    if (lane == 0) before = 0.0f;
+    if (lane == 63) sm.pmw[wave] = x;
+    __syncthreads();
+    float carry = 0.0f;
+    for (int w = 0; w < wave; ++w) carry = fmaxf(carry, sm.pmw[w]);
+    if (2 * tid < n) sm.pm[2 * tid] = fmaxf(fmaxf(carry, before), v0);
+    if (2 * tid + 1 < n) sm.pm[2 * tid + 1] = fmaxf(carry, x);
+    __syncthreads();
   }
   const uint16_t *rel_row = kKind == kBiasTable ? a.rel + (size_t)head * a.rel_extent : nullptr;
   const float rel_last = kKind == kBiasTable ? __uint_as_float((uint32_t)rel_row[a.rel_extent - 1] << 16) * kLog2e : 0.0f;
@@ -332,7 +370,9 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
         for (int cb = 0; cb < 2; ++cb) {
           const int r = cb * 16 + row;
           const int dmin = max(0, P0 + r - (j0 + kBlkKeys - 1));
-          const float ub = fmaf(fold, sm.qbound[wave][r], round_bf16_finite(slope * -(float)dmin) * kLog2e);
+          float qk = sm.qbound[wave][r];   // bounds |q . k| over the remaining keys
+          if (use_pm) qk = fminf(qk, sm.qnorm[wave][r] * sm.pm[blk - blk_lo]);
+          const float ub = fmaf(fold, qk, round_bf16_finite(slope * -(float)dmin) * kLog2e);
           ok = ok && (!head_ok || r >= ntok || ub <= m_run[cb] - kGap);
         }
         wdone = __ballot(!ok) == 0;
@@ -592,6 +632,57 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
   }
 }
 
+// Largest Euclidean norm of the stored key codes of each (sequence, KV head,
+// 128-key block), [batch][hkv][nblk]; keys at or past the sequence end do not
+// count, blocks past it are not written. One wave per block: load i brings
+// keys 8i .. 8i + 7 of the block (page i / 2), lane l chunk l % 8 of key
+// 8i + l / 8; the 8 lanes of a key add their squares. The norm is rounded up
+// by 1e-4 relative, which covers the fp32 sum of 128 squares (each square of
+// an e4m3 code is exact, each addition rounds by at most 2^-24).
+constexpr int kNormWaves = 4;
+__global__ __launch_bounds__(64 * kNormWaves) void key_norm_kernel(const uint8_t *kc, const int32_t *block_table,
+                                                                    int64_t bt_stride, const int32_t *seq_lens,
+                                                                    int batch, int hkv, int nblk, float *knorm) {
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * kNormWaves + (int)(threadIdx.x >> 6);   // (b * hkv + g) * nblk + blk
+  if (w >= batch * hkv * nblk) return;
+  const int blk = w % nblk;
+  const int g = (w / nblk) % hkv;
+  const int b = w / (nblk * hkv);
+  const int L = seq_lens[b];
+  if (blk * kBlkKeys >= L) return;
+  const int32_t *bt = block_table + (size_t)b * bt_stride;
+  const int pid = bt[min(blk * 8 + (lane & 7), (L - 1) >> 4)];
+  const size_t head_stride = (size_t)16 * kD;
+  const uint8_t *base = kc + (size_t)g * head_stride + (lane >> 3) * kD + 16 * (lane & 7);
+  v4u x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const size_t ph = (size_t)__builtin_amdgcn_readlane(pid, i >> 1);
+    x[i] = __builtin_nontemporal_load((const v4u *)(base + ph * hkv * head_stride + 8 * (i & 1) * kD));
+  }
+  float best = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float ss = 0.0f;
+    const uint32_t wv[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[c], false);
+      const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[c], true);
+      ss += (lo.x * lo.x + lo.y * lo.y) + (hi.x * hi.x + hi.y * hi.y);
+    }
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    ss += __shfl_xor(ss, 4, 64);
+    const int pos = blk * kBlkKeys + 8 * i + (lane >> 3);
+    if (pos < L) best = fmaxf(best, ss);
+  }
+#pragma unroll
+  for (int m = 8; m < 64; m <<= 1) best = fmaxf(best, __shfl_xor(best, m, 64));
+  if (lane == 0) knorm[w] = sqrtf(best) * 1.0001f;
+}
+
 }  // namespace
 
 hipError_t launch_prefill_e4m3(const PrefillE4M3Launch &a, hipStream_t s) {
@@ -606,8 +697,20 @@ hipError_t launch_prefill_e4m3(const PrefillE4M3Launch &a, hipStream_t s) {
   const size_t grid = (size_t)8 * (((size_t)units * nchunks + 7) / 8) * chunk;
   const dim3 g((unsigned)grid), b(64 * kPW);
   const int kind = a.slopes != nullptr ? kBiasSlope : (a.rel != nullptr ? kBiasTable : kBiasNone);
+  PrefillE4M3Launch pa = a;
+  // The key-norm pass reads every stored K byte of the batch once, so it runs
+  // only when enough query tiles share those bytes (at least 256 new tokens
+  // in the longest sequence); shorter calls keep the looser bound.
+  if (kind != kBiasSlope || a.max_q_len < 256) pa.knorm = nullptr;
+  if (pa.knorm != nullptr) {
+    const size_t waves = (size_t)a.batch * a.hkv * a.knorm_blocks;
+    hipLaunchKernelGGL(key_norm_kernel, dim3((unsigned)((waves + kNormWaves - 1) / kNormWaves)), dim3(64 * kNormWaves),
+                       0, s, a.kc, a.block_table, a.bt_stride, a.seq_lens, a.batch, a.hkv, a.knorm_blocks, a.knorm);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 #define KVQ_PREFILL_LAUNCH(K, P) \
-  hipLaunchKernelGGL((prefill_e4m3_kernel<K, P>), g, b, 0, s, a, tiles, units, head_blocks, chunk, nchunks)
+  hipLaunchKernelGGL((prefill_e4m3_kernel<K, P>), g, b, 0, s, pa, tiles, units, head_blocks, chunk, nchunks)
 #define KVQ_PREFILL_KINDS(P)                                   \
   do {                                                         \
     if (kind == kBiasSlope) KVQ_PREFILL_LAUNCH(kBiasSlope, P); \

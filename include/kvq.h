@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 6
+#define KVQ_ABI_VERSION 7
 
 /* A hipStream_t. NULL selects the null stream. */
 typedef struct ihipStream_t *kvq_stream_t;
@@ -354,8 +354,20 @@ int kvq_paged_attn_decode_noalloc(const kvq_cache *cache, const void *q,
  * bf16 [total_q][16][576] (not quantized), out bf16 [total_q][16][512], the
  * arithmetic of the NVFP4 decode; num_q_heads must be 16, max_seq_len at
  * most 32,768, window 0 and both biases NULL (KVQ_ERR_UNSUPPORTED
- * otherwise). No workspace is needed (workspace may be NULL,
- * workspace_bytes 0).
+ * otherwise).
+ *
+ * workspace (optional): with the e4m3 cache and per-head slopes, a workspace
+ * of at least kvq_prefill_workspace_bytes(...) bytes (4-byte aligned) lets
+ * the call first compute, for every (sequence, KV head, 128-key block), the
+ * largest Euclidean norm of the block's stored key codes (one extra launch
+ * reading the attended K bytes once). A tile then leaves its key walk as soon
+ * as |q . k| <= |q| |k| (Cauchy-Schwarz, over the codes) plus the bias at the
+ * nearest remaining distance puts every remaining score at least the zero cut
+ * below the running max, i.e. where every remaining probability rounds to
+ * exactly zero. Without it (NULL, or fewer bytes) the walk uses the looser
+ * bound 448 * sum |q|. The output is bit-identical either way; the workspace
+ * holds nothing the caller needs afterwards. Other cases need no workspace
+ * (workspace may be NULL, workspace_bytes 0).
  */
 int kvq_paged_attn_prefill(const kvq_cache *cache, const void *q, const int32_t *cu_q_lens,
                            int64_t total_q, int32_t max_q_len, const int32_t *block_table,
@@ -363,6 +375,15 @@ int kvq_paged_attn_prefill(const kvq_cache *cache, const void *q, const int32_t 
                            int32_t num_seqs, int32_t max_seq_len,
                            const kvq_attn_params *params, void *out, void *workspace,
                            size_t workspace_bytes, kvq_stream_t stream);
+
+/*
+ * Workspace (device bytes) that lets kvq_paged_attn_prefill bound the
+ * remaining scores by the per-block key norms: with the e4m3 cache and
+ * per-head slopes, 4 * num_seqs * num_kv_heads * ceil(max_seq_len / 128);
+ * 0 otherwise (and for invalid arguments, which the prefill call reports).
+ */
+size_t kvq_prefill_workspace_bytes(const kvq_cache *cache, int32_t num_seqs,
+                                   int32_t max_seq_len, const kvq_attn_params *params);
 
 /* Static text for a kvq_status value. */
 const char *kvq_status_str(int status);

@@ -246,3 +246,83 @@ def test_prefill_far_live_block_after_skipped_blocks(pmode):
                     rel_bias=tab, **mode)
     torch.cuda.synchronize()
     assert torch.equal(out, b)
+
+
+def test_prefill_key_norm_workspace():
+    """The slope-bias prefill's key-norm pass (white box): for every
+    (sequence, KV head, 128-key block) the workspace holds the largest
+    Euclidean norm of the block's stored key codes over keys before the
+    sequence end, never below the exact value (fp64 over the oracle's store)
+    and above it by at most 2e-4 relative. The output equals the one computed
+    without the workspace (the looser 448 * sum |q| bound) bit for bit."""
+    from oracle.codecs import e4m3_decode
+    c = make_attn_case("knorm", 78, [4096, 3000, 700], [300, 77, 700], 32, 4, 128,
+                       v_std=2.0, slopes=geometric_slopes(32))
+    dc = DeviceCase(c)
+    s = dc.calibrate()
+    dc.store_all(s)
+    B, G = len(c.seq_lens), c.num_kv_heads
+    nblk = (c.max_seq_len + 127) // 128
+    need = kvq.prefill_workspace_bytes(dc.cache, B, c.max_seq_len, c.num_q_heads, slopes=dc.slopes)
+    assert need == 4 * B * G * nblk
+    assert kvq.prefill_workspace_bytes(dc.cache, B, c.max_seq_len, c.num_q_heads) == 0   # no slopes
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    a = dc.prefill(s, workspace=ws)
+    b = dc.prefill(s, use_workspace=False)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(a.float()))
+    assert torch.equal(a, b)
+    got = ws.view(torch.float32).cpu().numpy().reshape(B, G, nblk)
+    kc, _ = oracle_cache(c, oracle_scales(c))
+    for bi, L in enumerate(c.seq_lens.tolist()):
+        pos = np.arange(L)
+        pages = c.block_table[bi][pos // 16]
+        for g in range(G):
+            codes = kc[pages, g, pos % 16, :]
+            norm = np.sqrt((e4m3_decode(codes).astype(np.float64) ** 2).sum(-1))
+            nb = (L + 127) // 128
+            want = np.array([norm[j * 128:(j + 1) * 128].max() for j in range(nb)])
+            have = got[bi, g, :nb].astype(np.float64)
+            assert np.all(have >= want), (bi, g, np.argmin(have - want))
+            assert np.all(have <= want * (1 + 2e-4)), (bi, g)
+
+
+@pytest.mark.parametrize("nq", [64, 300])
+def test_prefill_far_live_block_with_key_norms(nq):
+    """The planted far key (far_live_case) with enough new tokens for the
+    key-norm pass (nq = 300) and without (nq = 64): its block's norm keeps
+    the early stop from firing above it; oracle parity and bit-equality with
+    the call that takes no workspace."""
+    c = make_attn_case("farlive_n", 92, [4096, 700], [nq, 40], 8, 1, 128,
+                       slopes=np.full(8, 0.05, dtype=np.float32))
+    q = c.q.float()
+    q[:, :, 0] += 5.0
+    c.q = q.to(torch.bfloat16)
+    k = c.k.float()
+    planted = int(np.nonzero((c.seq_of_token == 0) & (c.pos_of_token == 200))[0][0])
+    k[planted] = 0.0
+    k[planted, 0, 0] = 3000.0
+    c.k = k.to(torch.bfloat16)
+    dc, out, ref = run_case(c)
+    print(check_attention(out, ref, "far live block, %d new tokens" % nq))
+    s = dc.calibrate()
+    b = dc.prefill(s, use_workspace=False)
+    torch.cuda.synchronize()
+    assert torch.equal(out, b)
+
+
+def test_prefill_key_norms_poisoned_pool():
+    """Pages past every sequence end poisoned with e4m3 NaN codes, slope bias,
+    enough new tokens for the key-norm pass: outputs finite, deterministic and
+    equal to the call without the workspace."""
+    c = make_attn_case("kpoison", 43, [700, 300, 16], [300, 280, 3], 16, 2, 128, spare_frac=2.0,
+                       slopes=geometric_slopes(16))
+    dc = DeviceCase(c, fill=0x7F)
+    s = dc.calibrate()
+    dc.store_all(s)
+    a = dc.prefill(s)
+    b = dc.prefill(s)
+    n = dc.prefill(s, use_workspace=False)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(a.float()))
+    assert torch.equal(a, b) and torch.equal(a, n)
