@@ -139,7 +139,8 @@ constexpr float zero_gap() { return kPMode == kPF16 ? 26.0f : 19.0f; }
 
 template <int kKind, int kPMode>
 __global__ __launch_bounds__(64 * kPW) __attribute__((amdgpu_waves_per_eu(2)))
-void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blocks, int chunk, int nchunks) {
+void prefill_e4m3_kernel(PrefillE4M3Launch a, int groups, int units, int head_blocks, int chunk, int nchunks,
+                         int tpw) {
   constexpr bool kP8 = kPMode != kPF16;
   constexpr float kGap = zero_gap<kPMode>();
   __shared__ PrefillSmem sm;
@@ -149,42 +150,57 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
   const int row = lane & 15;
   const int grp = lane >> 4;
 
-  // ---- work item (workgroup i runs on XCD i % 8). The tiles of a unit
-  // (sequence, KV head, head block) form nchunks chunks of `chunk` tiles;
-  // (unit, chunk) pairs go round-robin over the XCDs, so with 8 or more tiles
-  // every XCD holds one chunk of every unit (the same mix of units, whatever
-  // their cost), and each chunk's tiles stream the unit's K/V through one L2.
+  // ---- work item (workgroup i runs on XCD i % 8). A workgroup takes tpw
+  // consecutive 32-token tiles (a tile group) of kPW / tpw query heads of one
+  // KV head: wave w has head (w % hpw) of its head block and tile (w / hpw)
+  // of its group. The tile groups of a unit (sequence, KV head, head block)
+  // form nchunks chunks of `chunk` groups; (unit, chunk) pairs go round-robin
+  // over the XCDs, so with 8 or more groups every XCD holds one chunk of
+  // every unit (the same mix of units, whatever their cost), and each chunk's
+  // groups stream the unit's K/V through one L2.
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
   const int slot = bid >> 3;
   const int pair = (slot / chunk) * 8 + xcd;
   const int u = pair / nchunks;
-  const int tile = (pair - u * nchunks) * chunk + slot % chunk;
-  if (u >= units || tile >= tiles) return;
+  const int tg = (pair - u * nchunks) * chunk + slot % chunk;
+  if (u >= units || tg >= groups) return;
+  const int hpw = kPW / tpw;   // query heads per workgroup
   // Units are numbered KV head outermost, the last KV head first: under the
   // slope bias of the ALiBi family the slopes fall with the head index, so
   // the last heads reach farthest back before their probabilities vanish and
   // cost the most; dispatching them first leaves the cheap units for the end
   // (otherwise the last costly workgroups started late set the kernel's end).
   // Without a slope bias every unit costs about the same and the order does
-  // not matter.
-  const int hb = u % head_blocks;
-  const int b = (u / head_blocks) % a.batch;
+  // not matter. Within a KV head the head blocks also run last first, and
+  // the sequences are innermost: units of one head come together, so
+  // consecutive workgroups cost about the same. (Each XCD hands its
+  // workgroups to its shader engines in turn and in order; runs of equal
+  // cost keep one engine's long workgroups from holding back the dispatch
+  // of the next ones while other engines sit idle.)
+  const int b = u % a.batch;
+  const int hb = head_blocks - 1 - (u / a.batch) % head_blocks;
   const int g = a.hkv - 1 - u / (head_blocks * a.batch);
   const int q0 = a.cu_q_lens[b];
   const int lq = a.cu_q_lens[b + 1] - q0;
-  if (tile * kTileTok >= lq) return;
+  const int tile0 = tg * tpw;                     // the group's first tile
+  if (tile0 * kTileTok >= lq) return;
   const int L = a.seq_lens[b];
-  const int ntok = min(kTileTok, lq - tile * kTileTok);
+  const int tile = tile0 + wave / hpw;            // this wave's tile
+  const int ntok = max(0, min(kTileTok, lq - tile * kTileTok));   // 0: the wave has no query
   const int P0 = L - lq + tile * kTileTok;        // position of the tile's first token
   const int group = a.hq / a.hkv;
-  const int hloc = hb * kPW + wave;
+  const int hloc = hb * hpw + wave % hpw;
   const bool head_ok = hloc < group;
   const int head = g * group + (head_ok ? hloc : 0);
 
-  // keys [klo, khi): the union of the tile rows' ranges
-  const int khi = P0 + ntok;
-  const int klo = a.window > 0 ? max(0, P0 - a.window + 1) : 0;
+  // keys of the workgroup [klo, khi): the union of its rows' ranges (its
+  // tokens end at the sequence end at the latest); of this wave [wklo, wkhi)
+  const int P0g = L - lq + tile0 * kTileTok;
+  const int khi = min(P0g + tpw * kTileTok, L);
+  const int klo = a.window > 0 ? max(0, P0g - a.window + 1) : 0;
+  const int wkhi = P0 + ntok;
+  const int wklo = a.window > 0 ? max(0, P0 - a.window + 1) : 0;
   const int blk_lo = klo >> 7;
   const int blk_hi = (khi - 1) >> 7;              // inclusive
   const int page_last = (L - 1) >> 4;
@@ -396,8 +412,10 @@ void prefill_e4m3_kernel(PrefillE4M3Launch a, int tiles, int units, int head_blo
       for (int h = 0; h < 2; ++h) ids[h] = ids_n[h];
     }
     if (kKind == kBiasSlope && wdone) continue;
+    // a block outside this wave's keys (the workgroup's tiles reach further)
+    if (!head_ok || j0 >= wkhi || j0 + kBlkKeys <= wklo) continue;
 
-    const bool edge = (j0 + kBlkKeys - 1 > P0) || (a.window > 0 && j0 < khi - a.window);
+    const bool edge = (j0 + kBlkKeys - 1 > P0) || (a.window > 0 && j0 < wkhi - a.window);
     // ---- S^T = K Q^T for both column blocks, sharing every K operand read.
     // Lane (row, grp) gets keys kidx = 32*grp + 16*(j/4) + 4*(j%4) + i of
     // query row cb*16 + row.
@@ -688,15 +706,23 @@ __global__ __launch_bounds__(64 * kNormWaves) void key_norm_kernel(const uint8_t
 hipError_t launch_prefill_e4m3(const PrefillE4M3Launch &a, hipStream_t s) {
   if (a.d != kD) return hipErrorNotSupported;
   const int group = a.hq / a.hkv;
-  const int head_blocks = (group + kPW - 1) / kPW;
-  const int units = a.batch * a.hkv * head_blocks;
   const int tiles = (a.max_q_len + kTileTok - 1) / kTileTok;
   if (tiles == 0) return hipSuccess;
-  const int chunk = tiles >= 8 ? (tiles + 7) / 8 : tiles;   // tiles per chunk
-  const int nchunks = (tiles + chunk - 1) / chunk;
+  const int kind = a.slopes != nullptr ? kBiasSlope : (a.rel != nullptr ? kBiasTable : kBiasNone);
+  // Tiles per workgroup. Under the slope bias each head stops its key walk at
+  // its own distance (the smaller the slope, the later), and a workgroup
+  // runs until its last wave stops: one head and up to 8 tiles per
+  // workgroup keeps all of its waves busy to the end. Otherwise 8 heads of
+  // one tile.
+  const int tpw = kind != kBiasSlope ? 1 : (tiles >= 8 ? 8 : (tiles >= 4 ? 4 : (tiles >= 2 ? 2 : 1)));
+  const int hpw = kPW / tpw;
+  const int head_blocks = (group + hpw - 1) / hpw;
+  const int units = a.batch * a.hkv * head_blocks;
+  const int groups = (tiles + tpw - 1) / tpw;
+  const int chunk = groups >= 8 ? (groups + 7) / 8 : groups;   // tile groups per chunk
+  const int nchunks = (groups + chunk - 1) / chunk;
   const size_t grid = (size_t)8 * (((size_t)units * nchunks + 7) / 8) * chunk;
   const dim3 g((unsigned)grid), b(64 * kPW);
-  const int kind = a.slopes != nullptr ? kBiasSlope : (a.rel != nullptr ? kBiasTable : kBiasNone);
   PrefillE4M3Launch pa = a;
   // The key-norm pass reads every stored K byte of the batch once, so it runs
   // only when enough query tiles share those bytes (at least 256 new tokens
@@ -710,7 +736,7 @@ hipError_t launch_prefill_e4m3(const PrefillE4M3Launch &a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
 #define KVQ_PREFILL_LAUNCH(K, P) \
-  hipLaunchKernelGGL((prefill_e4m3_kernel<K, P>), g, b, 0, s, pa, tiles, units, head_blocks, chunk, nchunks)
+  hipLaunchKernelGGL((prefill_e4m3_kernel<K, P>), g, b, 0, s, pa, groups, units, head_blocks, chunk, nchunks, tpw)
 #define KVQ_PREFILL_KINDS(P)                                   \
   do {                                                         \
     if (kind == kBiasSlope) KVQ_PREFILL_LAUNCH(kBiasSlope, P); \
