@@ -136,7 +136,7 @@ kvq::MlaPlan plan_mla(int32_t num_seqs, int32_t max_seq_len, const kvq_attn_para
   const int64_t target = static_cast<int64_t>(current_cu_count());   // one workgroup per CU
   int64_t splits = p->num_splits > 0 ? p->num_splits : (target + num_seqs - 1) / (num_seqs > 0 ? num_seqs : 1);
   // at least 4 pages (64 keys) per split, at most 512 (the kernel stages a
-  // split's block-table slice in LDS); at most 64 splits (the combine)
+  // split's block-table slice in LDS); at most 64 splits (each adds a partial the combine reads)
   const int64_t max_splits = (pages + 3) / 4;
   if (splits > max_splits) splits = max_splits;
   if (splits > 64) splits = 64;

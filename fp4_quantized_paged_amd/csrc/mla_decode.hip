@@ -599,56 +599,53 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeMlaLaunch a,
 }
 
 // Split combine: per (sequence, head), out = 2^(E - M) * sum_s 2^(E_s - E) O_s
-// / sum_s 2^(M_s - M) den_s. Splits that saw no key (M_s = -inf, den_s = 0)
-// and splits with no nonzero term (E_s = -inf) drop out. One thread per 4
-// dims; the first splits' partials are requested with the split statistics.
+// / sum_s 2^(M_s - M) den_s, summed in split order. Splits that saw no key
+// (M_s = -inf, den_s = 0) and splits with no nonzero term (E_s = -inf) drop
+// out. One thread per 4 dims.
 constexpr int kCombineThreads = kLat / 4;
-constexpr int kMaxCombineSplits = 64;
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const float *part_o, const float *part_ml,
                                                                       uint16_t *out, int batch, int splits) {
-  __shared__ float s_w[2][kMaxCombineSplits];   // per split: O weight, denominator weight
-  __shared__ float s_f;                          // 2^(E - M) / den, or 0
   int b, h;
   xcd_local(blockIdx.x, batch, kHeads, b, h);    // on the XCD that wrote sequence b's partials
   const int bh = b * kHeads + h;
   const int t = threadIdx.x;
   const float *ml = part_ml + (size_t)bh * splits * 4;
   const float *po = part_o + (size_t)bh * splits * kLat + 4 * t;
-  // the first kPre splits' partials are requested together with the split
-  // statistics (one memory round trip); clamped copies past the last split
-  // are not used
+  // Every thread requests the split statistics (the same addresses for the
+  // whole workgroup) and its dims' partials of the first kPre splits in one
+  // memory round trip, then weighs them itself in split order: no exchange
+  // between threads. Clamped copies past the last split are not used.
   constexpr int kPre = 8;
-  v4f pre[kPre];
+  v4f pre[kPre], st[kPre];
 #pragma unroll
-  for (int s = 0; s < kPre; ++s) pre[s] = *(const v4f *)(po + (size_t)min(s, splits - 1) * kLat);
-  if (t < 64) {
-    float M = -INFINITY, E = -INFINITY;
-    const v4f r = t < splits ? *(const v4f *)(ml + 4 * t) : v4f{-INFINITY, 0.f, -INFINITY, 0.f};
-    M = r[0];
-    E = r[2];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      M = fmaxf(M, __shfl_xor(M, m, 64));
-      E = fmaxf(E, __shfl_xor(E, m, 64));
-    }
-    float wd = 0.0f, wo = 0.0f;
-    if (t < splits) {
-      if (r[0] != -INFINITY) wd = __builtin_amdgcn_exp2f(r[0] - M) * r[1];
-      if (r[2] != -INFINITY) wo = __builtin_ldexpf(1.0f, max((int)(r[2] - E), -200));
-      s_w[0][t] = wo;
-    }
-    float den = wd;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) den += __shfl_xor(den, m, 64);
-    if (t == 0) s_f = (den > 0.0f && E != -INFINITY) ? __builtin_ldexpf(1.0f / den, (int)(E - M)) : 0.0f;
+  for (int s = 0; s < kPre; ++s) {
+    const int c = min(s, splits - 1);
+    st[s] = *(const v4f *)(ml + 4 * c);
+    pre[s] = *(const v4f *)(po + (size_t)c * kLat);
   }
-  __syncthreads();
-  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  float M = -INFINITY, E = -INFINITY;
 #pragma unroll
   for (int s = 0; s < kPre; ++s)
-    if (s < splits) acc += s_w[0][s] * pre[s];
-  for (int s = kPre; s < splits; ++s) acc += s_w[0][s] * *(const v4f *)(po + (size_t)s * kLat);
-  const float f = s_f;
+    if (s < splits) {
+      M = fmaxf(M, st[s][0]);
+      E = fmaxf(E, st[s][2]);
+    }
+  for (int s = kPre; s < splits; ++s) {
+    const v4f r = *(const v4f *)(ml + 4 * s);
+    M = fmaxf(M, r[0]);
+    E = fmaxf(E, r[2]);
+  }
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  float den = 0.0f;
+  auto add = [&](const v4f &r, const v4f &o) {
+    if (r[0] != -INFINITY) den += __builtin_amdgcn_exp2f(r[0] - M) * r[1];
+    if (r[2] != -INFINITY) acc += __builtin_ldexpf(1.0f, max((int)(r[2] - E), -200)) * o;
+  };
+#pragma unroll
+  for (int s = 0; s < kPre; ++s)
+    if (s < splits) add(st[s], pre[s]);
+  for (int s = kPre; s < splits; ++s) add(*(const v4f *)(ml + 4 * s), *(const v4f *)(po + (size_t)s * kLat));
+  const float f = (den > 0.0f && E != -INFINITY) ? __builtin_ldexpf(1.0f / den, (int)(E - M)) : 0.0f;
   uint2 w;
   w.x = f32_to_bf16_bits(acc[0] * f) | (f32_to_bf16_bits(acc[1] * f) << 16);
   w.y = f32_to_bf16_bits(acc[2] * f) | (f32_to_bf16_bits(acc[3] * f) << 16);
