@@ -13,9 +13,11 @@
 //
 // Kernel design (gfx950, wave64, 8 waves per workgroup):
 //  * a workgroup owns 32 consecutive new tokens of one sequence and up to 8
-//    query heads of one KV head (one wave per head); every wave holds two
-//    16-token column blocks, so one staged K/V block feeds 16 QK^T MFMAs and
-//    32 PV MFMAs per wave;
+//    query heads of one KV head (one wave per head); under the slope bias it
+//    owns one query head and up to 8 consecutive 32-token tiles instead (one
+//    wave per tile), so that its waves stop at about the same block. Every
+//    wave holds two 16-token column blocks, so one staged K/V block feeds 16
+//    QK^T MFMAs and 32 PV MFMAs per wave;
 //  * K/V advance in 128-key blocks (8 pages). The workgroup copies a block's K
 //    rows (bank-swizzled) and its token-minor V^T pages, converted once to
 //    fp16, into LDS while the next block's bytes are already in flight in
@@ -42,12 +44,15 @@
 //    unchanged;
 //    with the slope bias (non-negative slopes) a wave stops altogether once
 //    a bound on every remaining score lies that far below the running max:
-//    |q . k| <= 448 * sum |q| (448 is the e4m3 maximum) and the bias only
-//    falls with distance; the workgroup leaves the key loop when all of its
-//    waves have stopped;
-//  * workgroups are numbered so that all tiles of one (sequence, KV head) land
-//    on the same XCD (dispatch is round-robin over the 8 XCDs), where they
-//    stream the same K/V blocks through that XCD's L2.
+//    |q . k| <= 448 * sum |q| (448 is the e4m3 maximum), or, given the
+//    per-block key norms that key_norm_kernel writes first, |q| times the
+//    largest remaining key norm (Cauchy-Schwarz), and the bias only falls
+//    with distance; the workgroup leaves the key loop when all of its waves
+//    have stopped;
+//  * the tile groups of each unit are spread over the 8 XCDs in chunks (the
+//    same mix of units on every XCD), and units are ordered costliest first
+//    with the sequences innermost, so that consecutive workgroups of an XCD,
+//    which go to its shader engines in turn, cost about the same.
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
