@@ -229,6 +229,24 @@ def test_prefill_validation(lib):
              FAKE, None, 0, None) == 0                            # no queries: no launch
 
 
+def test_prefill_workspace_bytes(lib):
+    """kvq_prefill_workspace_bytes: one fp32 key norm per (sequence, KV head,
+    128-key block) with slopes on the e4m3 cache; 0 without slopes, for the
+    NVFP4 format, for empty or invalid arguments."""
+    d = e4m3_desc()
+    q = lib.kvq_prefill_workspace_bytes
+    assert q(ctypes.byref(d), 3, 1000, ctypes.byref(params(alibi_slopes=FAKE))) == 4 * 3 * 4 * 8
+    assert q(ctypes.byref(d), 3, 1024, ctypes.byref(params(alibi_slopes=FAKE))) == 4 * 3 * 4 * 8
+    assert q(ctypes.byref(d), 3, 1025, ctypes.byref(params(alibi_slopes=FAKE))) == 4 * 3 * 4 * 9
+    assert q(ctypes.byref(d), 3, 1000, ctypes.byref(params())) == 0
+    assert q(ctypes.byref(d), 0, 1000, ctypes.byref(params(alibi_slopes=FAKE))) == 0
+    assert q(ctypes.byref(d), 3, 0, ctypes.byref(params(alibi_slopes=FAKE))) == 0
+    assert q(ctypes.byref(d), 3, 1000, ctypes.byref(params(num_q_heads=31, alibi_slopes=FAKE))) == 0
+    assert q(ctypes.byref(d), 3, 1000, None) == 0
+    nv = kvq.CacheDesc(2, 16, 1, 576, 64, FAKE, None)
+    assert q(ctypes.byref(nv), 3, 1000, ctypes.byref(params(num_q_heads=16))) == 0
+
+
 def test_struct_layouts_match_header(tmp_path):
     """The ctypes mirrors of kvq_cache and kvq_attn_params have the header's
     field offsets and sizes (checked by compiling offsetof/sizeof with gcc)."""
