@@ -39,6 +39,9 @@ CASES = [
     ([260, 90], [70, 90], 12, 3, 0, True),           # group 4: half the waves idle
     ([200], [45], 32, 2, 0, True),                   # group 16: two head blocks
     ([100, 50, 33], [0, 50, 0], 8, 2, 0, True),      # sequences without new tokens
+    ([500, 40], [20, 7], 16, 2, 0, True),            # slope bias, one tile: 8 heads per workgroup
+    ([300, 290], [256, 250], 16, 4, 0, True),        # slope bias, 8 tiles: one head per workgroup, key norms
+    ([1200], [300], 8, 1, 100, True),                # slope bias, window, key norms
 ]
 
 
