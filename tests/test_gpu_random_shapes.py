@@ -75,3 +75,41 @@ def test_random_prefill(seed):
     ref = paged_prefill(c.q.float().numpy(), c.cu_q_lens, kc, vc, c.block_table, c.seq_lens, c.softmax_scale,
                         so["q"], so["k"], so["v"], c.window, c.slopes, rel=c.rel)
     print(check_attention(out, ref, "prefill %s q %s h%d/%d w%d %s %s" % (lens, qlens, hq, hkv, window, kind, mode)))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_nvfp4_decode_and_prefill(seed):
+    """NVFP4 records: random batch, lengths (0 to 6,000 keys), layer std and
+    RoPE scale, planned or forced splits for the decode, then a prefill of a
+    random number of each sequence's last tokens over the same records."""
+    from oracle.nvfp4 import new_pool, store_records, mla_decode, mla_prefill
+    from workloads import make_mla_case, bf16
+    import fp4_quantized_paged_amd as kvq
+    rng = np.random.default_rng(9300 + seed)
+    B = int(rng.integers(1, 6))
+    lens = [int(x) for x in rng.integers(0, 6000, B)]
+    std = float(rng.choice([0.05, 0.5, 1.0, 4.0]))
+    rope = float(rng.choice([0.5, 1.0, 2.0]))
+    splits = int(rng.choice([0, 0, 1, 5, 24]))
+    c = make_mla_case("rnv", 9300 + seed, lens, layer_std=std, rope_scale=rope)
+    cache = kvq.Nvfp4Cache(c.num_pages)
+    kvq.store(cache, c.kv.cuda(), None, torch.from_numpy(c.slot_mapping).cuda(), c.rope_scale)
+    bt = torch.from_numpy(c.block_table).cuda()
+    sl = torch.from_numpy(c.seq_lens).cuda()
+    out = kvq.decode(cache, c.q.cuda(), bt, sl, c.max_seq_len, c.softmax_scale, k_scale=c.rope_scale,
+                     num_splits=splits)
+    q_lens = np.array([int(rng.integers(0, min(n, 300) + 1)) for n in lens], dtype=np.int32)
+    if q_lens.sum() == 0:
+        q_lens[int(np.argmax(lens))] = min(max(lens), 1)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    qp = bf16(rng.standard_normal((int(cu[-1]), 16, 576)).astype(np.float32))
+    outp = kvq.prefill(cache, qp.cuda(), torch.from_numpy(cu).cuda(), max(int(q_lens.max()), 1), bt, sl,
+                       c.max_seq_len, c.softmax_scale, k_scale=c.rope_scale)
+    torch.cuda.synchronize()
+    pool = new_pool(c.num_pages)
+    store_records(pool, c.kv.float().numpy(), c.slot_mapping, c.rope_scale)
+    ref = mla_decode(c.q.float().numpy(), pool, c.block_table, c.seq_lens, c.softmax_scale, c.rope_scale)
+    print(check_attention(out, ref, "nvfp4 decode %s std %g rope %g splits %d" % (lens, std, rope, splits)))
+    if cu[-1] > 0:
+        refp = mla_prefill(qp.float().numpy(), cu, pool, c.block_table, c.seq_lens, c.softmax_scale, c.rope_scale)
+        print(check_attention(outp, refp, "nvfp4 prefill %s q %s" % (lens, q_lens.tolist())))
