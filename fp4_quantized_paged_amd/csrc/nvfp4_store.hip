@@ -21,10 +21,10 @@
 // [296,304) zero; [304,368) RoPE codes.
 //
 // One 32-lane half of a wave handles one token per pass, one lane per
-// 16-element group (plus two RoPE elements per lane); the loads of both
-// passes are issued before either token is encoded. The records are assembled
-// in LDS and leave as 23 16-byte stores each, with the slots kept in LDS; the
-// 16 records of a workgroup (a whole page in a bulk store) are contiguous.
+// 16-element group (plus two RoPE elements per lane); the loads of every pass
+// are issued before any token is encoded. The records are assembled in LDS
+// and leave as 23 16-byte stores each, with the slots kept in LDS; the records
+// of a workgroup (half a page in a bulk store) are contiguous.
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -37,23 +37,24 @@ namespace {
 constexpr int kRec = 368;
 constexpr int kThreads = 256;
 constexpr int kHalves = kThreads / 32;    // half waves: one token each per pass
-constexpr int kPasses = 2;                // tokens per half wave (1 and 4 measured slower)
+constexpr int kPasses = 1;                // tokens per half wave (2: same bulk rate, slower short stores; 4: slower)
 constexpr int kTokensPerBlock = kHalves * kPasses;
 
-// e2m1 code (0..7) of a magnitude already clipped to [0, 6], round to nearest
-// even code: the grid is evenly spaced inside each binade, so rint on the
-// scaled magnitude (ties to even) is the even code.
-__device__ __forceinline__ uint32_t e2m1_code(float a) {
-  const float c0 = __builtin_rintf(a * 2.0f);          // 0, .5, 1, 1.5, 2 -> 0..4
-  const float c1 = __builtin_rintf(a) + 2.0f;          // 2, 3, 4 -> 4..6
-  const float c2 = __builtin_rintf(a * 0.5f) + 4.0f;   // 4, 6 -> 6, 7
-  const float c = a < 2.0f ? c0 : (a < 4.0f ? c1 : c2);
-  return (uint32_t)c;
-}
+// Eight values (the four bf16 pairs of w) times r as e2m1 codes, element 2i
+// in the low nibble of byte i: clipped to [-6, 6] (med3 keeps the sign of a
+// zero), then the gfx950 fp4 conversion with a unit scale, which rounds to the
+// nearest code, ties to the even one, and keeps the sign bit (the same result
+// as rint on the magnitude scaled per binade: the grid is evenly spaced inside
+// each binade).
+__device__ __forceinline__ float clip6(float y) { return __builtin_amdgcn_fmed3f(y, -6.0f, 6.0f); }
 
-__device__ __forceinline__ uint32_t e2m1_encode(float y) {
-  const float a = fminf(fabsf(y), 6.0f);
-  return e2m1_code(a) | ((__float_as_uint(y) >> 28) & 8u);   // sign bit kept
+__device__ __forceinline__ uint32_t e2m1x8(const uint32_t *w, float r) {
+  uint32_t p = 0u;
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, clip6(bf16lo(w[0]) * r), clip6(bf16hi(w[0]) * r), 1.0f, 0);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, clip6(bf16lo(w[1]) * r), clip6(bf16hi(w[1]) * r), 1.0f, 1);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, clip6(bf16lo(w[2]) * r), clip6(bf16hi(w[2]) * r), 1.0f, 2);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, clip6(bf16lo(w[3]) * r), clip6(bf16hi(w[3]) * r), 1.0f, 3);
+  return p;
 }
 
 // One token's record, from its already loaded elements, into LDS.
@@ -85,12 +86,8 @@ __device__ __forceinline__ void encode_token(const StoreNvfp4Launch &a, uint4 x0
   // ---- e2m1 codes, two per byte (element 2i low nibble)
   uint32_t packed[2] = {0u, 0u};
   if (dg != 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t lo = e2m1_encode(bf16lo(w[i]) * r);
-      const uint32_t hi = e2m1_encode(bf16hi(w[i]) * r);
-      packed[i >> 2] |= (lo | (hi << 4)) << (8 * (i & 3));
-    }
+    packed[0] = e2m1x8(w, r);
+    packed[1] = e2m1x8(w + 4, r);
   }
   // ---- RoPE pair through the e4m3 store quantizer
   const uint32_t rope = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(bf16lo(rp) * a.rope_inv),
