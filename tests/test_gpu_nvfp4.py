@@ -16,7 +16,9 @@ pytestmark = pytest.mark.gpu
 
 def special_tokens():
     """Edge tokens: all zero, an exact two-level grid token (amax 168), a
-    token with an all-zero group, tiny magnitudes, huge magnitudes."""
+    token whose e2m1 inputs sit exactly on the rounding midpoints and one bf16
+    step either side of them, a token with an all-zero group, tiny
+    magnitudes, huge magnitudes."""
     rng = np.random.default_rng(17)
     toks = []
     toks.append(np.zeros(576, np.float32))
@@ -25,6 +27,17 @@ def special_tokens():
     t[0:16] = np.tile(grid, 2) * 28.0
     t[0] = 168.0
     t[16:32] = np.tile(grid, 2) * 0.125
+    t[512:] = rng.standard_normal(64).astype(np.float32)
+    toks.append(t)
+    # amax 2688 makes the outer scale 1; groups 1 and 2 have amax 48, so their
+    # scale is 8 and x / 8 is exact: group 1 lands on every midpoint of the
+    # e2m1 grid (ties go to the even code) and rounds -0.5 / 8 to a signed
+    # zero; group 2 sits one bf16 step either side of midpoints and of 6
+    t = np.zeros(576, np.float32)
+    t[0] = 2688.0
+    t[16:32] = [2, -2, 6, -6, 10, -10, 14, -14, 20, -20, 28, -28, 40, -40, 48, -0.5]
+    t[32:48] = [19.875, 20.125, -19.875, -20.125, 1.9921875, 2.015625, 39.75, 40.25,
+                27.875, 28.125, 48, -48, 5.96875, 6.03125, 13.9375, 14.0625]
     t[512:] = rng.standard_normal(64).astype(np.float32)
     toks.append(t)
     t = rng.standard_normal(576).astype(np.float32)

@@ -55,6 +55,26 @@ def test_exact_grid_token_amax_168():
     assert np.all(z == 0)
 
 
+def test_midpoint_token_rounds_ties_to_even_codes():
+    # amax 2688 -> s2 = 1; groups 1 and 2 have amax 48 -> scale 8 (code 0x50)
+    # and x / 8 is exact. Group 1 sits on the e2m1 midpoints 0.25, 0.75, 1.25,
+    # 1.75, 2.5, 3.5 and 5: round to nearest, ties to the even code
+    # (0, 2, 2, 4, 4, 6, 6), signs kept, -0.5 / 8 a negative zero (code 8).
+    # Group 2 sits one bf16 step either side of midpoints and of 6.
+    x = np.zeros((1, 576), np.float32)
+    x[0, 0] = 2688.0
+    x[0, 16:32] = [2, -2, 6, -6, 10, -10, 14, -14, 20, -20, 28, -28, 40, -40, 48, -0.5]
+    x[0, 32:48] = [19.875, 20.125, -19.875, -20.125, 1.9921875, 2.015625, 39.75, 40.25,
+                   27.875, 28.125, 48, -48, 5.96875, 6.03125, 13.9375, 14.0625]
+    assert np.array_equal(bf16_round(x), x)
+    rec = encode_records(x)
+    assert record_s2(rec)[0] == np.float32(1.0)
+    assert rec[0, OFF_GSCALE + 1] == 0x50 and rec[0, OFF_GSCALE + 2] == 0x50
+    codes = np.stack([rec[0, :256] & 15, rec[0, :256] >> 4], axis=1).reshape(-1)
+    assert codes[16:32].tolist() == [0, 8, 2, 10, 2, 10, 4, 12, 4, 12, 6, 14, 6, 14, 7, 8]
+    assert codes[32:48].tolist() == [4, 5, 12, 13, 0, 1, 6, 7, 5, 6, 7, 15, 1, 2, 3, 4]
+
+
 def test_power_of_two_invariance():
     rng = np.random.default_rng(1)
     x = token(rng, 1.3, 64)
