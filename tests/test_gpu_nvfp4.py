@@ -253,6 +253,63 @@ def test_store_static_outer_scale_bit_exact(outer):
     assert bad.size == 0, bad[:10]
 
 
+def e2m1_input_tokens(seed: int):
+    """Every bf16 value of magnitude 2^-10 up to 48, both signs, spread in a
+    seeded random order over groups whose first element is +-48. Element 0 of
+    each token is 2688, so the outer scale is exactly 1; every other group has
+    amax 48, so its scale is 8 (exact in e4m3) and x / 8 is exact: the e2m1
+    inputs are every bf16-representable value of magnitude up to 6, each
+    rounding midpoint and its neighbours among them."""
+    mags = []
+    for e in range(-10, 6):
+        m = (1.0 + np.arange(128) / 128.0) * 2.0 ** e
+        mags.append(m[m <= 48.0])
+    mags = np.concatenate(mags).astype(np.float32)
+    vals = np.concatenate([mags, -mags])
+    rng = np.random.default_rng(seed)
+    vals = vals[rng.permutation(vals.size)]
+    per_token = 31 * 15                       # groups 1..31, 15 free slots each
+    T = (vals.size + per_token - 1) // per_token
+    x = np.zeros((T, 576), np.float32)
+    x[:, 0] = 2688.0
+    lat = x[:, 16:512].reshape(T, 31, 16)
+    lat[:, :, 0] = np.where(rng.random((T, 31)) < 0.5, 48.0, -48.0)
+    free = np.zeros(T * per_token, np.float32)
+    free[:vals.size] = vals
+    lat[:, :, 1:] = free.reshape(T, 31, 15)
+    x[:, 16:512] = lat.reshape(T, 496)
+    x[:, 512:] = x[:, 16:80]
+    return x
+
+
+@pytest.mark.parametrize("outer", [None, 1.0, 2.0 ** -20])
+def test_store_every_e2m1_input_bit_exact(outer):
+    """Every bf16 value up to the e2m1 maximum as an e2m1 input through the
+    NVFP4 store, bit-exact against the oracle: with the per-token outer scale,
+    with a static one of 1 (the same inputs), and with a tiny static one that
+    saturates the group scales at 448 and sends the inputs far past 6 (clip)."""
+    x = e2m1_input_tokens(9)
+    assert np.array_equal(bf16_round(x), x)
+    T = x.shape[0]
+    num_pages = (T + 15) // 16 + 1
+    slot = np.random.default_rng(6).permutation(num_pages * 16)[:T].astype(np.int64)
+    cache = kvq.Nvfp4Cache(num_pages)
+    xs, ss = bf16(x).cuda(), torch.from_numpy(slot).cuda()
+    if outer is None:
+        kvq.store(cache, xs, None, ss, 1.0)
+    else:
+        kvq.store_nvfp4_static(cache, xs, ss, 1.0, outer)
+    torch.cuda.synchronize()
+    pool = new_pool(num_pages)
+    if outer is None:
+        store_records(pool, x, slot, 1.0)
+    else:
+        store_records(pool, x, slot, 1.0, static_s2=outer)
+    got = cache.records.cpu().numpy()
+    bad = np.argwhere(got != pool)
+    assert bad.size == 0, bad[:10]
+
+
 def test_static_outer_scale_ab_through_decode():
     """A/B of the outer scale through the GPU store and MLA decode: relative
     L2 error of the decode output against attention over the unquantized
